@@ -1,0 +1,9 @@
+"""The oracle against its pins (CPU only)."""
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(orc, pin):
+    pin(orc)
