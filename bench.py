@@ -1,0 +1,204 @@
+"""Throughput benchmark of the QSA hot path on one MI355X.
+
+One step = qsa_index_topk -> qsa_attend -> qsa_merge over a batch of B
+independent problems (seeded synthetic caches already resident in HBM).
+The default workload is the decode step (1 token, 24 x 256 query heads,
+2 KV heads, 8192 cached cells, index dim 128, top-2048) over B = 256
+independent caches, so the working set (~2.7 GB) is far larger than the
+256 MB last-level cache and every step streams from HBM.
+
+Prints one JSON line: metric/value (kept KV cells attended per second),
+per-stage times from HIP events recorded on the launch stream, algorithmic
+HBM bytes and flops, the roofline of the dominant kernel, and the oracle's
+single-thread throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selected KV cells attended/sec + achieved HBM GB/s (% of 8 TB/s), 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+# fp32 FMA peak without packed-fp32 instructions: 256 CUs x 4 SIMDs x 16 lanes
+# x 2 flop x 2.4 GHz.
+FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12   # 78.6
+
+WORKLOADS = {
+    # name: (datagen config, default batch, description)
+    "decode": ("decode", 256, "decode step: 1 token, 24x256 q heads, 2 KV heads, 8192 cells, "
+                              "index dim 128, top-2048, int8 KV + fp16 scale per 32"),
+    "draft": ("draft", 32, "draft batch: 8 tokens, 24x256 q heads, 2 KV heads, 65536 cells, "
+                           "top-2048 per token"),
+    "long": ("long", 16, "long context: 1 token, 24x256 q heads, 2 KV heads, 262144 cells, "
+                         "top-2048, planted heavy-tail index scores"),
+    "prompt": ("prompt", 1, "prompt chunk: 2048 tokens vs 65536 cells, fp16 q/out, "
+                            "top-2048 per token"),
+    "tiny": ("tiny", 1024, "tiny: 1 token, 4x64 q heads, 1 KV head, 512 cells, top-128"),
+}
+
+
+def algorithmic_bytes(p: dict, B: int, n_sel_total: int) -> dict:
+    """Bytes the method must move per step (no reuse across tokens):
+    index keys of every visible cell once per call (when any token selects),
+    the kept cells' K/V codes and scales once per token, q, ids, output."""
+    T, N, di, Hq, Hkv, D, k = p["T"], p["N"], p["di"], p["Hq"], p["Hkv"], p["D"], p["k"]
+    pos0 = p.get("pos0", N - T)
+    nvis_max = pos0 + T
+    qbytes = 2 if p["q_dtype"] == "f16" else 4
+    obytes = 2 if p["out_dtype"] == "f16" else 4
+    selects = nvis_max > p["dense_max"] and nvis_max > k
+    index = B * (nvis_max * di * 2 + T * di * 2) if selects else 0
+    per_cell = Hkv * (D + (D // 32) * 2) * 2          # K and V codes + scales
+    attend = n_sel_total * (per_cell + 4) + B * T * Hq * D * qbytes
+    out = B * T * Hq * D * obytes
+    return dict(index=index, attend=attend, out=out, total=index + attend + out)
+
+
+def attend_flops(p: dict, n_sel_total: int) -> float:
+    return float(n_sel_total) * p["Hq"] * p["D"] * 4      # QK + PV FMAs, 2 flop each
+
+
+def cpu_baseline(inp_cfg: str, target_s: float, P: int) -> dict:
+    """The oracle (plain C, double, one thread) on as many problems of the same
+    workload as fit in about target_s seconds."""
+    from datagen import make_inputs
+    from oracle.oracle import default
+    orc = default()
+    done, cells, t_used = 0, 0, 0.0
+    seed = 9000
+    while t_used < target_s:
+        inp = make_inputs(inp_cfg, seed=seed + done, batch=1)
+        if inp_cfg == "prompt":   # one token of the chunk per sample
+            t = done % inp["T"]
+            inp.update(T=1, pos0=inp["pos0"] + t, q_idx=inp["q_idx"][:, t:t + 1],
+                       q=inp["q"][:, t:t + 1])
+        t0 = time.perf_counter()
+        r = orc.run(inp, P=P, scale=1.0 / math.sqrt(inp["D"]))
+        t_used += time.perf_counter() - t0
+        cells += int(r["n_sel"].sum())
+        done += 1
+    unit = "cells/s"
+    what = "token" if inp_cfg == "prompt" else "problem"
+    return dict(value=cells / t_used, unit=unit, cores=1, kind="oracle",
+                sample=f"{done} {what}(s) of the {inp_cfg} workload, index+attend+merge, "
+                       f"{t_used:.1f} s single-threaded")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--P", type=int, default=None)
+    ap.add_argument("--distinct", type=int, default=8,
+                    help="distinct seeded problems, tiled to the batch on the GPU")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import top_sparse_attention_score_amd as qsa
+    from datagen import make_inputs
+
+    cfg_name, default_batch, desc = WORKLOADS[args.workload]
+    B = args.batch or default_batch
+    nd = max(1, min(args.distinct, B))
+    print(f"[bench] workload={args.workload} B={B} distinct={nd}", file=sys.stderr, flush=True)
+    base = make_inputs(cfg_name, seed=1234, batch=nd)
+    P = args.P or base["P"]
+    reps = math.ceil(B / nd)
+    dev = {}
+    for key in ("q_idx", "K_idx", "q", "Kq", "Ksc", "Vq", "Vsc"):
+        t = torch.from_numpy(base[key]).cuda()
+        dev[key] = t.repeat((reps,) + (1,) * (t.dim() - 1))[:B].contiguous()
+    inp = dict(base)
+    inp["batch"] = B
+    path = qsa.path_for(inp, P=P)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        path.run(dev)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start = time.perf_counter()
+    for s in range(K):
+        e = evs[s]
+        e[0].record(stream)
+        path.index(dev["q_idx"], dev["K_idx"])
+        e[1].record(stream)
+        path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"])
+        e[2].record(stream)
+        path.merge()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage = np.zeros(3)
+    for e in evs:
+        for i in range(3):
+            stage[i] += e[i].elapsed_time(e[i + 1])
+    stage_ms = stage / K
+    step_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / K
+
+    n_sel_total = int(path.n_sel.sum().item())
+    by = algorithmic_bytes(inp, B, n_sel_total)
+    flops = attend_flops(inp, n_sel_total)
+    cells_per_s = n_sel_total / (step_ms * 1e-3)
+    gbs = by["total"] / (step_ms * 1e-3) / 1e9
+
+    # Dominant kernel: the stage with the largest average time.
+    names = ["index_topk", "attend", "merge"]
+    dom = int(np.argmax(stage_ms))
+    if names[dom] == "attend":
+        achieved = flops / (stage_ms[1] * 1e-3) / 1e12
+        roof = dict(kernel="k_attend", bound="alu", achieved=round(achieved, 2),
+                    peak=round(FP32_VALU_PEAK_TFLOPS, 1), unit="TFLOP/s",
+                    frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4), traffic=None,
+                    hbm_gbs=round(by["attend"] / (stage_ms[1] * 1e-3) / 1e9, 1))
+    else:
+        sb = by["index"] if names[dom] == "index_topk" else by["out"]
+        achieved = sb / (stage_ms[dom] * 1e-3) / 1e9
+        roof = dict(kernel=names[dom], bound="hbm", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=None)
+
+    line = {
+        "metric": METRIC, "value": cells_per_s, "unit": "cells/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": desc, "batch": B, "T": inp["T"], "n_cells": inp["N"],
+                   "k": inp["k"], "P": P, "d_idx": inp["di"], "heads": f"{inp['Hq']}x{inp['D']}",
+                   "kv_heads": inp["Hkv"]},
+        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": by["total"],
+        "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(names, stage_ms)},
+        "wall_s": round(wall, 3),
+        "roofline": roof,
+    }
+    if inp["q_dtype"] == "f16":
+        line["dtype"] = "f16 in, f32 accumulate"
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg_name, args.cpu_seconds, P)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

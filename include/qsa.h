@@ -1,0 +1,197 @@
+/*
+ * qsa.h -- C ABI of the MI355X (gfx950) QSA top-k sparse attention library
+ * (libqsa.so).
+ *
+ * QSA, as the audit pages describe it, attends each query token to a small
+ * selected subset of a long KV cache:
+ *   1. an indexer scores every visible cached cell against the token and
+ *      keeps the top-k ("opus r15 track A: prompt_chunk wave zipping, fused
+ *      alpha|beta GEMM, QSA PSO pre-warm, 24 GB chunk 2048", "what changed"
+ *      item 1: qsa_score_mm / qsa_topk, used once a prompt exceeds 2051
+ *      tokens; "Round 5 Track C Report: Direct FP16 qcurh in qsa_prep +
+ *      PromptGemm Dead Buffer Removal & Layer-Local Aliasing", section 1
+ *      Target 2: 2051 selected-id words per token);
+ *   2. softmax attention over only the kept cells of an int8 KV cache with
+ *      fp16 scales, split into chunks that each produce a (max, sum,
+ *      unnormalised output) partial ("opus r20 track A: MTP map mlock +
+ *      qsa_attn / qsa_merge decode tweaks", section 2 "qsa.metal", qsa_attn;
+ *      section 3 "verification": random int8 KV with fp16 scales);
+ *   3. a log-sum-exp merge of the chunk partials (same page, section 2,
+ *      qsa_merge).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing, keeps no state between calls and never
+ *     synchronises; every call only enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and returns.
+ *   - Arguments are validated on the host before anything is enqueued.  An
+ *     invalid call returns a negative qsa_status and enqueues nothing.  A
+ *     kernel launch failure returns QSA_ERR_HIP.  There is no device-side
+ *     error reporting: contents (ids out of range, NaN scores) are not
+ *     checked.
+ *   - Calls are thread-safe (no global mutable state).
+ *   - B = `batch` independent problems are processed by one call; problem b
+ *     reads and writes the b-th slice of every tensor.
+ *   - fp16 means IEEE binary16.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define QSA_API __attribute__((visibility("default")))
+#else
+#define QSA_API
+#endif
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or shape */
+    QSA_ERR_UNSUPPORTED = -2,  /* valid, but no kernel variant for it */
+    QSA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+    QSA_ERR_HIP = -4           /* a kernel launch failed */
+} qsa_status;
+
+typedef enum { QSA_F32 = 0, QSA_F16 = 1 } qsa_dtype;
+
+/* Static description of a status code (never NULL). */
+QSA_API const char* qsa_status_string(int status);
+
+/* QSA_VERSION of the built library. */
+QSA_API int qsa_version(void);
+
+/* ------------------------------------------------------------------------
+ * qsa_index_topk -- index score + top-k selection.
+ *
+ * Token t of problem b sits at position pos[t] = pos0 + t and sees the cells
+ * 0..pos[t] (causal, own cell included).  Its score against visible cell j
+ * is the dot product of its fp16 index query with the cell's fp16 index key,
+ * accumulated in fp32 (fp16 products are exact in fp32).  If the token sees
+ * at most dense_max cells, or at most k, all visible cells are kept (the
+ * dense fallback below the 2051-cell bound named in the r15 audit page);
+ * otherwise the k highest-scoring visible cells are kept, equal scores going
+ * to the lower cell index.
+ *
+ * Inputs
+ *   q_idx  fp16 [B][T][d_idx]      16-byte aligned
+ *   K_idx  fp16 [B][N][d_idx]      16-byte aligned
+ * Outputs
+ *   ids    int32 [B][T][ids_cap]   kept cell ids in ascending order, then -1
+ *   n_sel  int32 [B][T]            number of kept cells of each token
+ * Workspace
+ *   ws     device scratch of at least qsa_index_topk_workspace(desc) bytes,
+ *          16-byte aligned; its contents on entry do not matter.
+ *
+ * Selection is exact on fp32 scores: ids equal a full sort by (score desc,
+ * index asc) of the fp32 scores.  With index inputs on a grid where fp32
+ * accumulation is exact (e.g. multiples of 2^-5 in [-4, 4] with d_idx <=
+ * 1024) this is the exact-arithmetic selection.
+ *
+ * Supported: d_idx in {64, 128}; 1 <= k <= ids_cap; 0 <= dense_max <=
+ * ids_cap; 0 <= pos0; pos0 + T <= N; 1 <= batch <= 65535.
+ * --------------------------------------------------------------------- */
+typedef struct qsa_index_desc {
+    int batch;      /* B */
+    int T;          /* query tokens per problem */
+    int n_cells;    /* N cached cells per problem */
+    int d_idx;      /* index key dimension */
+    int k;          /* cells kept per token */
+    int pos0;       /* position of token 0 */
+    int dense_max;  /* keep every visible cell while visible <= dense_max */
+    int ids_cap;    /* row length of ids (>= max(k, dense_max)) */
+} qsa_index_desc;
+
+QSA_API size_t qsa_index_topk_workspace(const qsa_index_desc* desc);
+
+QSA_API int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const void* K_idx,
+                   int32_t* ids, int32_t* n_sel, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_attend -- split-KV attention partials over the kept cells
+ * ("opus r20 ..." page, section 2, qsa_attn).
+ *
+ * Query head h reads KV head g = h / (Hq / Hkv).  The ids row of token t is
+ * cut into P contiguous chunks of S = ceil(n_sel[t] / P) ids; chunk c covers
+ * row positions [c*S, min((c+1)*S, n_sel[t])) and may be empty.  For chunk c
+ * and head h, with x_j = scale * sum_d q[h][d] * Kq[j][g][d] * Ksc[j][g][d/32]:
+ *   m = max_j x_j,   l = sum_j exp(x_j - m),
+ *   o[d] = sum_j exp(x_j - m) * Vq[j][g][d] * Vsc[j][g][d/32]   (unnormalised)
+ * An empty chunk gives m = -inf, l = 0, o = 0.  Arithmetic is fp32.
+ *
+ * Inputs
+ *   q      [B][T][Hq][D], fp32 (q_dtype QSA_F32) or fp16 (QSA_F16), 16-byte
+ *          aligned
+ *   Kq,Vq  int8 codes; cell j of KV head g of problem b starts at
+ *          base + b*batch_stride + j*cell_stride + g*D        (bytes)
+ *   Ksc,Vsc fp16 scales, one per 32 elements; the scales of (b, j, g) start
+ *          at base + b*batch_stride + j*cell_stride + g*(D/32)*2 (bytes)
+ *          Dense default layouts: Kq/Vq [B][N][Hkv][D], Ksc/Vsc
+ *          [B][N][Hkv][D/32]; a stride of 0 selects the dense default, so a
+ *          caller may also interleave codes and scales of a cell.
+ *   ids    int32 [B][T][ids_cap], n_sel int32 [B][T] (as written by
+ *          qsa_index_topk, or any ids in [0, N) -- out-of-range ids are
+ *          undefined behaviour).  Row entries at or beyond n_sel[t] are never
+ *          read.
+ * Output
+ *   partials  float, qsa_partials_floats(desc) elements, 16-byte aligned:
+ *             m [B][T][Hq][P] at offset 0,
+ *             l [B][T][Hq][P] at offset B*T*Hq*P,
+ *             o [B][T][Hq][P][D] at offset 2*B*T*Hq*P.
+ *
+ * Supported: D in {64, 256}; Hq % Hkv == 0 with Hq/Hkv in {1,2,4,8,12,16};
+ * 1 <= P <= 64; n_sel[t] <= ids_cap; all four cache base pointers and
+ * batch strides 16-byte aligned; Kq/Vq cell strides multiples of 16;
+ * Ksc/Vsc cell strides multiples of 4; 1 <= batch*T <= 2^31-1.
+ * --------------------------------------------------------------------- */
+typedef struct qsa_attn_desc {
+    int batch;           /* B */
+    int T;               /* query tokens per problem */
+    int Hq;              /* query heads */
+    int Hkv;             /* KV heads */
+    int D;               /* head dimension */
+    int P;               /* split-KV chunks per token */
+    int ids_cap;         /* row length of ids */
+    int n_cells;         /* N, cells per problem (sizes the default batch strides) */
+    float scale;         /* softmax scale, e.g. 1/sqrt(D) */
+    int q_dtype;         /* qsa_dtype of q */
+    int out_dtype;       /* qsa_dtype of the merged output */
+    long long kq_cell_stride, ksc_cell_stride, vq_cell_stride, vsc_cell_stride;
+    long long kq_batch_stride, ksc_batch_stride, vq_batch_stride, vsc_batch_stride;
+} qsa_attn_desc;
+
+QSA_API size_t qsa_partials_floats(const qsa_attn_desc* desc);
+
+QSA_API int qsa_attend(const qsa_attn_desc* desc, const void* q, const int8_t* Kq,
+               const void* Ksc, const int8_t* Vq, const void* Vsc,
+               const int32_t* ids, const int32_t* n_sel, float* partials,
+               void* stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_merge -- log-sum-exp merge of the P chunk partials
+ * ("opus r20 ..." page, section 2, qsa_merge).
+ *   M = max_c m_c;  e_c = exp(m_c - M);  L = sum_c l_c e_c  (fma, c order);
+ *   out[d] = (sum_c o_c[d] e_c) / L   (fma in c order, then one division)
+ * A row whose chunks are all empty writes 0.
+ *
+ * Input   partials as written by qsa_attend with the same desc.
+ * Output  out [B][T][Hq][D], fp32 or fp16 (round to nearest even) per
+ *         desc->out_dtype, 16-byte aligned.
+ * Supported: as qsa_attend.
+ * --------------------------------------------------------------------- */
+QSA_API int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* out,
+              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path (through the C ABI) against the double-precision
+oracle on seeded inputs of the five workloads, the pos0 x ntok sweep of the
+pages' bitwise check, attention-only runs on random scattered ids, and the
+pages' bit-exact claims (zero padding, exact max, determinism)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from datagen import make_inputs, scattered_ids, sweep_cases
+from tests.gpu_util import (assert_ids_equal, assert_out_close, assert_partials_close,
+                            run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def _oracle_all(orc, inp, P):
+    return orc.run(inp, P=P, scale=1.0 / math.sqrt(inp["D"]))
+
+
+# ------------------------------------------------------------ workloads ---
+
+@pytest.mark.parametrize("cfg,batch", [("tiny", 3), ("decode", 2), ("draft", 1), ("long", 1)])
+def test_workload_parity(orc, cfg, batch):
+    inp = make_inputs(cfg, seed=1000 + batch, batch=batch)
+    say(f"[parity] {cfg} B={batch} T={inp['T']} N={inp['N']} P={inp['P']}")
+    res = run_gpu(inp)
+    ref = _oracle_all(orc, inp, inp["P"])
+    assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+    assert_partials_close(res, ref["pm"], ref["pl"], ref["po"])
+    assert_out_close(res["out"], ref["out"])
+
+
+def test_prompt_chunk_sampled(orc):
+    """The 2048-token prompt chunk at full size on the GPU; the oracle checks
+    sampled tokens one by one, and every token's kept set is checked against
+    exact float64 scores (a property that holds at any size)."""
+    inp = make_inputs("prompt", seed=1005)
+    say("[parity] prompt T=2048 N=65536 full size")
+    res = run_gpu(inp)
+    T, pos0, k = inp["T"], inp["pos0"], inp["k"]
+    assert np.all(res["n_sel"] == k)
+    S = inp["q_idx"][0].astype(np.float64) @ inp["K_idx"][0].astype(np.float64).T
+    for t in range(T):
+        nvis = pos0 + t + 1
+        kept = res["ids"][0, t, :k]
+        assert np.all(np.diff(kept) > 0) and kept[0] >= 0 and kept[-1] < nvis
+        assert np.all(res["ids"][0, t, k:] == -1)
+        s = S[t, :nvis]
+        mask = np.zeros(nvis, bool)
+        mask[kept] = True
+        lo = s[mask].min()
+        assert s[~mask].max() <= lo, t
+        tie_out = np.flatnonzero(~mask & (s == lo))
+        if tie_out.size:
+            assert np.flatnonzero(mask & (s == lo)).max() < tie_out.min(), t
+    for t in (0, 1, 777, 1500, 2046, 2047):
+        one = dict(inp)
+        one.update(T=1, pos0=pos0 + t, q_idx=inp["q_idx"][:, t:t + 1], q=inp["q"][:, t:t + 1])
+        ref = _oracle_all(orc, one, 1)
+        assert_ids_equal(res["ids"][:, t:t + 1], res["n_sel"][:, t:t + 1], ref["ids"],
+                         ref["n_sel"])
+        assert_out_close(res["out"][:, t:t + 1], ref["out"], f"token {t}")
+
+
+def test_pos_sweep(orc):
+    """pos0 in {0,1,63,64,512,2047,2048,2050,8192,30000} x ntok in {1,2,4,8}
+    on a 32768-cell cache: dense fallback, the 2051 bound and top-k."""
+    for pos0, ntok in sweep_cases():
+        inp = make_inputs("decode", seed=2000 + pos0 + ntok, N=32768, T=ntok, pos0=pos0)
+        say(f"[sweep] pos0={pos0} ntok={ntok}")
+        res = run_gpu(inp)
+        ref = _oracle_all(orc, inp, inp["P"])
+        assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+        assert_out_close(res["out"], ref["out"], f"pos0={pos0} ntok={ntok}")
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16, 64])
+def test_split_counts(orc, P):
+    inp = make_inputs("decode", seed=3000 + P, batch=1)
+    say(f"[split] P={P}")
+    res = run_gpu(inp, P=P)
+    ref = _oracle_all(orc, inp, P)
+    assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+    assert_partials_close(res, ref["pm"], ref["pl"], ref["po"])
+    assert_out_close(res["out"], ref["out"])
+
+
+@pytest.mark.parametrize("n_max", [1, 5, 64, 65, 300, 2051])
+def test_attend_scattered_ids(orc, n_max):
+    """Attention and merge alone on random scattered ids (decoupled from the
+    indexer), per the pages' bitwise-check input."""
+    inp = make_inputs("decode", seed=4000 + n_max, batch=2, N=32768, T=4, pos0=30000)
+    ids, n_sel = scattered_ids(seed=5, batch=2, T=4, N=32768, cap=inp["cap"], pos0=30000,
+                               n_max=n_max)
+    say(f"[scattered] n_max={n_max}")
+    res = run_gpu(inp, ids=ids, n_sel=n_sel, index=False)
+    pm, pl, po = orc.attend(inp["q"], inp["Kq"], inp["Ksc"], inp["Vq"], inp["Vsc"], ids,
+                            n_sel, P=inp["P"], scale=1 / 16)
+    assert_partials_close(res, pm, pl, po)
+    assert_out_close(res["out"], orc.merge(pm, pl, po))
+
+
+def test_tiny_fp16_and_gqa_variants(orc):
+    """Every supported (G, D) pair with fp32 and fp16 queries on small inputs."""
+    for D in (64, 256):
+        for G in (1, 2, 4, 8, 12, 16):
+            for qd in ("f32", "f16"):
+                Hkv = 2 if G <= 8 else 1
+                cfg = dict(T=2, N=700, di=64, k=150, dense_max=153, Hq=G * Hkv, Hkv=Hkv,
+                           D=D, P=3, q_dtype=qd, out_dtype=qd, heavy_tail=False)
+                inp = make_inputs(cfg, seed=G * 10 + D)
+                say(f"[variant] D={D} G={G} q={qd}")
+                res = run_gpu(inp)
+                ref = _oracle_all(orc, inp, 3)
+                assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+                assert_out_close(res["out"], ref["out"], f"D={D} G={G} {qd}")
+
+
+def test_tie_stress(orc):
+    """40 identical index keys straddle rank 128 of a 512-cell cache: the kept
+    ids must give the tie quota to the lowest indices, bit-exactly."""
+    inp = make_inputs("tiny", seed=77, batch=2)
+    rng = np.random.default_rng(78)
+    for b in range(2):
+        s = inp["q_idx"][b, 0].astype(np.float64) @ inp["K_idx"][b].astype(np.float64).T
+        order = np.lexsort((np.arange(512), -s))
+        group = rng.choice(order[100:160], size=40, replace=False)
+        inp["K_idx"][b, group] = inp["K_idx"][b, order[128]]
+    res = run_gpu(inp)
+    ref = _oracle_all(orc, inp, inp["P"])
+    assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+    assert_out_close(res["out"], ref["out"])
+
+
+def test_all_scores_equal(orc):
+    """q_idx = 0: every visible cell scores 0, so top-k is the k lowest ids."""
+    inp = make_inputs("decode", seed=79)
+    inp["q_idx"][:] = 0
+    res = run_gpu(inp)
+    assert res["n_sel"][0, 0] == 2048
+    assert np.array_equal(res["ids"][0, 0, :2048], np.arange(2048))
+    ref = _oracle_all(orc, inp, inp["P"])
+    assert_out_close(res["out"], ref["out"])
+
+
+def test_interleaved_cache_layout(orc):
+    """Codes and scales of a cell interleaved in one buffer via the strides
+    give the same result as the dense layout."""
+    inp = make_inputs("decode", seed=80, batch=2, N=4096)
+    B, N, Hkv, D = 2, 4096, 2, 256
+    rec = Hkv * D + Hkv * (D // 32) * 2          # 544 bytes: codes, then scales
+    buf = {}
+    for name, codes, scales in (("K", inp["Kq"], inp["Ksc"]), ("V", inp["Vq"], inp["Vsc"])):
+        raw = np.zeros((B, N, rec), dtype=np.uint8)
+        raw[:, :, :Hkv * D] = codes.reshape(B, N, -1).view(np.uint8)
+        raw[:, :, Hkv * D:] = scales.reshape(B, N, -1).view(np.uint8)
+        buf[name] = torch.from_numpy(raw).cuda()
+    strides = dict(kq_cell_stride=rec, ksc_cell_stride=rec, vq_cell_stride=rec,
+                   vsc_cell_stride=rec, kq_batch_stride=N * rec, ksc_batch_stride=N * rec,
+                   vq_batch_stride=N * rec, vsc_batch_stride=N * rec)
+    import top_sparse_attention_score_amd as qsa
+    dev = qsa.to_device(inp)
+    path = qsa.path_for(inp, strides=strides)
+    path.index(dev["q_idx"], dev["K_idx"])
+    Kb, Vb = buf["K"], buf["V"]
+    path.attend(dev["q"], Kb, Kb[:, :, Hkv * D:], Vb, Vb[:, :, Hkv * D:])
+    path.merge()
+    torch.cuda.synchronize()
+    dense = run_gpu(inp)
+    assert np.array_equal(path.out.cpu().numpy(), dense["out"])
+    ref = _oracle_all(orc, inp, inp["P"])
+    assert_out_close(dense["out"], ref["out"])
+
+
+# ------------------------------------------------ the pages' bit claims ---
+
+def test_padding_beyond_n_sel_is_ignored():
+    """Entries past n_sel never change the partials (an absent cell adds
+    p = 0): garbage padding gives bitwise-identical partials and output."""
+    inp = make_inputs("decode", seed=81, batch=2, N=16384, T=3, pos0=16000)
+    ids, n_sel = scattered_ids(seed=9, batch=2, T=3, N=16384, cap=inp["cap"], pos0=16000,
+                               n_max=1000)
+    a = run_gpu(inp, ids=ids, n_sel=n_sel, index=False)
+    ids2 = ids.copy()
+    rng = np.random.default_rng(10)
+    for b in range(2):
+        for t in range(3):
+            n = n_sel[b, t]
+            ids2[b, t, n:] = rng.integers(0, 16384, size=ids2.shape[-1] - n)
+    b_ = run_gpu(inp, ids=ids2, n_sel=n_sel, index=False)
+    for key in ("pm", "pl", "po", "out"):
+        assert a[key].tobytes() == b_[key].tobytes(), key
+
+
+def test_run_to_run_determinism():
+    inp = make_inputs("draft", seed=82, N=16384)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    for key in ("ids", "n_sel", "pm", "pl", "po", "out"):
+        assert a[key].tobytes() == b[key].tobytes(), key
+
+
+def test_position_zero_is_exact():
+    """A token at position 0 keeps only cell 0 and its output is that cell's
+    dequantised V row, bit for bit (exp(0) = 1, fma(1, v, 0) = v, v / 1 = v)."""
+    inp = make_inputs("decode", seed=83, batch=2, N=64, T=1, pos0=0)
+    res = run_gpu(inp)
+    assert np.all(res["n_sel"] == 1) and np.all(res["ids"][:, :, 0] == 0)
+    v = (inp["Vq"][:, 0].astype(np.float64) *
+         np.repeat(inp["Vsc"][:, 0].astype(np.float64), 32, axis=-1)).astype(np.float32)
+    G = inp["Hq"] // inp["Hkv"]
+    for h in range(inp["Hq"]):
+        assert res["out"][:, 0, h].tobytes() == v[:, h // G].tobytes()
+
+
+def test_chunk_max_is_exact_max_of_logits():
+    """The partial max of a one-cell chunk is that cell's logit, and the max
+    of a chunk equals the max over its one-cell chunks bit for bit."""
+    inp = make_inputs("decode", seed=84, batch=1, N=4096, T=1, pos0=4095, k=64,
+                      dense_max=67)
+    one = run_gpu(inp, P=64)          # 64 ids -> 64 one-cell chunks
+    whole = run_gpu(inp, P=1)
+    assert np.all(one["pl"] == 1.0)
+    assert whole["pm"][..., 0].tobytes() == one["pm"].max(axis=-1).tobytes()

@@ -1,0 +1,205 @@
+// qsa_api.hip -- the C ABI declared in include/qsa.h: argument validation,
+// defaults, and dispatch to the kernel launchers.  Every check happens on the
+// host before anything is enqueued; nothing here allocates or synchronises.
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "qsa.h"
+#include "qsa_launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_index(const qsa_index_desc* d)
+{
+    if (!d)
+        return QSA_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->T < 1 || d->n_cells < 1 || d->k < 1 || d->pos0 < 0 ||
+        d->dense_max < 0 || d->ids_cap < 1)
+        return QSA_ERR_INVALID_ARG;
+    if ((long long)d->pos0 + d->T > d->n_cells)
+        return QSA_ERR_INVALID_ARG;
+    if (d->k > d->ids_cap || d->dense_max > d->ids_cap)
+        return QSA_ERR_INVALID_ARG;
+    if (d->d_idx != 64 && d->d_idx != 128)
+        return QSA_ERR_UNSUPPORTED;
+    if (d->batch > 65535 || (long long)d->batch * d->T > INT_MAX)
+        return QSA_ERR_UNSUPPORTED;
+    return QSA_OK;
+}
+
+// Fills `L` from the descriptor (defaults for zero strides) and validates it.
+int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
+{
+    if (!d)
+        return QSA_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->T < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 32 || d->P < 1 ||
+        d->ids_cap < 1 || d->n_cells < 1)
+        return QSA_ERR_INVALID_ARG;
+    if (d->Hq % d->Hkv != 0 || d->D % 32 != 0 || !isfinite(d->scale))
+        return QSA_ERR_INVALID_ARG;
+    if ((d->q_dtype != QSA_F32 && d->q_dtype != QSA_F16) ||
+        (d->out_dtype != QSA_F32 && d->out_dtype != QSA_F16))
+        return QSA_ERR_INVALID_ARG;
+    if (d->P > 64)
+        return QSA_ERR_UNSUPPORTED;
+    if (!qsa::attend_supported(d->Hq / d->Hkv, d->D))
+        return QSA_ERR_UNSUPPORTED;
+    const long long bt = (long long)d->batch * d->T;
+    if (bt > INT_MAX || bt * d->Hq > INT_MAX || d->Hkv > 65535)
+        return QSA_ERR_UNSUPPORTED;
+
+    const long long row = (long long)d->Hkv * d->D;           // int8 codes per cell
+    const long long srow = (long long)d->Hkv * (d->D / 32) * 2;  // scale bytes per cell
+    L->kq_cs = d->kq_cell_stride ? d->kq_cell_stride : row;
+    L->vq_cs = d->vq_cell_stride ? d->vq_cell_stride : row;
+    L->ksc_cs = d->ksc_cell_stride ? d->ksc_cell_stride : srow;
+    L->vsc_cs = d->vsc_cell_stride ? d->vsc_cell_stride : srow;
+    L->kq_bs = d->kq_batch_stride ? d->kq_batch_stride : L->kq_cs * d->n_cells;
+    L->vq_bs = d->vq_batch_stride ? d->vq_batch_stride : L->vq_cs * d->n_cells;
+    L->ksc_bs = d->ksc_batch_stride ? d->ksc_batch_stride : L->ksc_cs * d->n_cells;
+    L->vsc_bs = d->vsc_batch_stride ? d->vsc_batch_stride : L->vsc_cs * d->n_cells;
+    if (L->kq_cs < 0 || L->vq_cs < 0 || L->ksc_cs < 0 || L->vsc_cs < 0 || L->kq_bs < 0 ||
+        L->vq_bs < 0 || L->ksc_bs < 0 || L->vsc_bs < 0)
+        return QSA_ERR_INVALID_ARG;
+    if (L->kq_cs % 16 || L->vq_cs % 16 || L->ksc_cs % 4 || L->vsc_cs % 4)
+        return QSA_ERR_INVALID_ARG;
+    if (L->kq_bs % 16 || L->vq_bs % 16 || L->ksc_bs % 16 || L->vsc_bs % 16)
+        return QSA_ERR_INVALID_ARG;
+
+    L->B = d->batch;
+    L->T = d->T;
+    L->Hq = d->Hq;
+    L->Hkv = d->Hkv;
+    L->D = d->D;
+    L->P = d->P;
+    L->cap = d->ids_cap;
+    L->N = d->n_cells;
+    L->scale = d->scale;
+    L->q_f16 = d->q_dtype == QSA_F16;
+    L->out_f16 = d->out_dtype == QSA_F16;
+    return QSA_OK;
+}
+
+size_t partial_rows(const qsa_attn_desc* d)
+{
+    return (size_t)d->batch * (size_t)d->T * (size_t)d->Hq * (size_t)d->P;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qsa_status_string(int status)
+{
+    switch (status) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_INVALID_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case QSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QSA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int qsa_version(void) { return QSA_VERSION; }
+
+size_t qsa_index_topk_workspace(const qsa_index_desc* desc)
+{
+    if (check_index(desc) != QSA_OK)
+        return 0;
+    return qsa::index_workspace_bytes(desc->batch, desc->T, desc->n_cells);
+}
+
+int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const void* K_idx,
+                   int32_t* ids, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream)
+{
+    const int st = check_index(desc);
+    if (st != QSA_OK)
+        return st;
+    if (!q_idx || !K_idx || !ids || !n_sel)
+        return QSA_ERR_INVALID_ARG;
+    if (!aligned(q_idx, 16) || !aligned(K_idx, 16) || !aligned(ids, 4) || !aligned(n_sel, 4))
+        return QSA_ERR_INVALID_ARG;
+    const size_t need = qsa::index_workspace_bytes(desc->batch, desc->T, desc->n_cells);
+    if (!ws || ws_bytes < need || !aligned(ws, 16))
+        return QSA_ERR_WORKSPACE;
+    qsa::IndexLaunch a;
+    a.B = desc->batch;
+    a.T = desc->T;
+    a.N = desc->n_cells;
+    a.DI = desc->d_idx;
+    a.k = desc->k;
+    a.pos0 = desc->pos0;
+    a.dense_max = desc->dense_max;
+    a.cap = desc->ids_cap;
+    a.q_idx = q_idx;
+    a.K_idx = K_idx;
+    a.ids = ids;
+    a.n_sel = n_sel;
+    a.keys = (uint32_t*)ws;
+    if (qsa::launch_index_topk(a, (hipStream_t)stream) != hipSuccess)
+        return QSA_ERR_HIP;
+    return QSA_OK;
+}
+
+size_t qsa_partials_floats(const qsa_attn_desc* desc)
+{
+    qsa::AttnLaunch L;
+    if (check_attn(desc, &L) != QSA_OK)
+        return 0;
+    const size_t rows = partial_rows(desc);
+    return 2 * rows + rows * (size_t)desc->D;
+}
+
+int qsa_attend(const qsa_attn_desc* desc, const void* q, const int8_t* Kq, const void* Ksc,
+               const int8_t* Vq, const void* Vsc, const int32_t* ids, const int32_t* n_sel,
+               float* partials, void* stream)
+{
+    qsa::AttnLaunch a;
+    const int st = check_attn(desc, &a);
+    if (st != QSA_OK)
+        return st;
+    if (!q || !Kq || !Ksc || !Vq || !Vsc || !ids || !n_sel || !partials)
+        return QSA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(Kq, 16) || !aligned(Ksc, 16) || !aligned(Vq, 16) ||
+        !aligned(Vsc, 16) || !aligned(ids, 4) || !aligned(n_sel, 4) || !aligned(partials, 16))
+        return QSA_ERR_INVALID_ARG;
+    const size_t rows = partial_rows(desc);
+    a.q = q;
+    a.Kq = Kq;
+    a.Ksc = Ksc;
+    a.Vq = Vq;
+    a.Vsc = Vsc;
+    a.ids = ids;
+    a.n_sel = n_sel;
+    a.pm = partials;
+    a.pl = partials + rows;
+    a.po = partials + 2 * rows;
+    a.out = nullptr;
+    if (qsa::launch_attend(a, (hipStream_t)stream) != hipSuccess)
+        return QSA_ERR_HIP;
+    return QSA_OK;
+}
+
+int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* out, void* stream)
+{
+    qsa::AttnLaunch a;
+    const int st = check_attn(desc, &a);
+    if (st != QSA_OK)
+        return st;
+    if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16))
+        return QSA_ERR_INVALID_ARG;
+    const size_t rows = partial_rows(desc);
+    a.pm = (float*)partials;
+    a.pl = (float*)partials + rows;
+    a.po = (float*)partials + 2 * rows;
+    a.out = out;
+    if (qsa::launch_merge(a, (hipStream_t)stream) != hipSuccess)
+        return QSA_ERR_HIP;
+    return QSA_OK;
+}
+
+}  // extern "C"

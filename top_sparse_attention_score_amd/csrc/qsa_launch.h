@@ -1,0 +1,51 @@
+// qsa_launch.h -- host-side launchers of the QSA kernels (internal).
+// Arguments are validated by the C-ABI layer before these are called; each
+// launcher only enqueues kernels and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct IndexLaunch {
+    int B, T, N, DI, k, pos0, dense_max, cap;
+    const void* q_idx;
+    const void* K_idx;
+    int32_t* ids;
+    int32_t* n_sel;
+    uint32_t* keys;  // workspace: [B][T][N] score keys
+};
+
+// Bytes of workspace the index path needs.
+size_t index_workspace_bytes(int B, int T, int N);
+
+hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s);
+
+struct AttnLaunch {
+    int B, T, Hq, Hkv, D, P, cap, N;
+    float scale;
+    bool q_f16, out_f16;
+    const void* q;
+    const int8_t* Kq;
+    const void* Ksc;
+    const int8_t* Vq;
+    const void* Vsc;
+    long long kq_cs, ksc_cs, vq_cs, vsc_cs;  // cell strides, bytes
+    long long kq_bs, ksc_bs, vq_bs, vsc_bs;  // batch strides, bytes
+    const int32_t* ids;
+    const int32_t* n_sel;
+    float* pm;
+    float* pl;
+    float* po;
+    void* out;
+};
+
+// True if a kernel variant exists for (G, D, q dtype).
+bool attend_supported(int G, int D);
+
+hipError_t launch_attend(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_merge(const AttnLaunch& a, hipStream_t s);
+
+}  // namespace qsa

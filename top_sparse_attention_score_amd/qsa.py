@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libqsa.so (the C ABI in include/qsa.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, builds the C descriptor, and passes raw device pointers and
+torch's current HIP stream to the library.  All computation happens in the
+library's HIP kernels.  There is no fallback: if libqsa.so is missing or a
+call is rejected, a QsaError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+QSA_F32 = 0
+QSA_F16 = 1
+
+_c_int, _c_ll, _c_float, _vp = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p
+
+
+class QsaError(RuntimeError):
+    pass
+
+
+class IndexDesc(ctypes.Structure):
+    _fields_ = [("batch", _c_int), ("T", _c_int), ("n_cells", _c_int), ("d_idx", _c_int),
+                ("k", _c_int), ("pos0", _c_int), ("dense_max", _c_int), ("ids_cap", _c_int)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", _c_int), ("T", _c_int), ("Hq", _c_int), ("Hkv", _c_int),
+                ("D", _c_int), ("P", _c_int), ("ids_cap", _c_int), ("n_cells", _c_int),
+                ("scale", _c_float), ("q_dtype", _c_int), ("out_dtype", _c_int),
+                ("kq_cell_stride", _c_ll), ("ksc_cell_stride", _c_ll),
+                ("vq_cell_stride", _c_ll), ("vsc_cell_stride", _c_ll),
+                ("kq_batch_stride", _c_ll), ("ksc_batch_stride", _c_ll),
+                ("vq_batch_stride", _c_ll), ("vsc_batch_stride", _c_ll)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqsa.so once (raises QsaError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QsaError(f"{LIB_PATH} is missing: build it with "
+                           "top_sparse_attention_score_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.qsa_status_string.argtypes = [_c_int]
+        L.qsa_status_string.restype = ctypes.c_char_p
+        L.qsa_version.restype = _c_int
+        L.qsa_index_topk_workspace.argtypes = [ctypes.POINTER(IndexDesc)]
+        L.qsa_index_topk_workspace.restype = ctypes.c_size_t
+        L.qsa_index_topk.argtypes = [ctypes.POINTER(IndexDesc), _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]
+        L.qsa_index_topk.restype = _c_int
+        L.qsa_partials_floats.argtypes = [ctypes.POINTER(AttnDesc)]
+        L.qsa_partials_floats.restype = ctypes.c_size_t
+        L.qsa_attend.argtypes = [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp]
+        L.qsa_attend.restype = _c_int
+        L.qsa_merge.argtypes = [ctypes.POINTER(AttnDesc), _vp, _vp, _vp]
+        L.qsa_merge.restype = _c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().qsa_status_string(code).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise QsaError(f"{what}: {status_string(code)} ({code})")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+# ----------------------------------------------------------- descriptors ---
+
+def index_desc(*, batch: int, T: int, n_cells: int, d_idx: int, k: int, pos0: int,
+               dense_max: int, ids_cap: int) -> IndexDesc:
+    return IndexDesc(batch, T, n_cells, d_idx, k, pos0, dense_max, ids_cap)
+
+
+def attn_desc(*, batch: int, T: int, Hq: int, Hkv: int, D: int, P: int, ids_cap: int,
+              n_cells: int, scale: float | None = None, q_dtype: int = QSA_F32,
+              out_dtype: int = QSA_F32, strides: dict | None = None) -> AttnDesc:
+    """Attention descriptor; `strides` may set any of the *_cell_stride /
+    *_batch_stride fields (bytes); unset ones keep the dense default."""
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    d = AttnDesc(batch, T, Hq, Hkv, D, P, ids_cap, n_cells, sc, q_dtype, out_dtype)
+    for key, val in (strides or {}).items():
+        setattr(d, key, int(val))
+    return d
+
+
+def qsa_index_topk_workspace(desc: IndexDesc) -> int:
+    return int(lib().qsa_index_topk_workspace(ctypes.byref(desc)))
+
+
+def qsa_partials_floats(desc: AttnDesc) -> int:
+    return int(lib().qsa_partials_floats(ctypes.byref(desc)))
+
+
+# ----------------------------------------------------------------- calls ---
+
+def qsa_index_topk(desc: IndexDesc, q_idx, K_idx, ids, n_sel, ws, stream=None) -> None:
+    _check(lib().qsa_index_topk(ctypes.byref(desc), _ptr(q_idx), _ptr(K_idx), _ptr(ids),
+                                _ptr(n_sel), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)), "qsa_index_topk")
+
+
+def qsa_attend(desc: AttnDesc, q, Kq, Ksc, Vq, Vsc, ids, n_sel, partials,
+               stream=None) -> None:
+    _check(lib().qsa_attend(ctypes.byref(desc), _ptr(q), _ptr(Kq), _ptr(Ksc), _ptr(Vq),
+                            _ptr(Vsc), _ptr(ids), _ptr(n_sel), _ptr(partials),
+                            _stream(stream)), "qsa_attend")
+
+
+def qsa_merge(desc: AttnDesc, partials, out, stream=None) -> None:
+    _check(lib().qsa_merge(ctypes.byref(desc), _ptr(partials), _ptr(out), _stream(stream)),
+           "qsa_merge")
+
+
+# ------------------------------------------------------- whole-path plan ---
+
+class QsaPath:
+    """Device buffers for one workload shape plus the three calls in order.
+
+    Holds only torch-allocated device memory (inputs are passed in already on
+    the GPU); run() enqueues index_topk -> attend -> merge on one stream.
+    """
+
+    def __init__(self, *, batch, T, N, di, k, pos0, dense_max, cap, Hq, Hkv, D, P,
+                 q_f16=False, out_f16=False, scale=None, device="cuda", strides=None):
+        self.idesc = index_desc(batch=batch, T=T, n_cells=N, d_idx=di, k=k, pos0=pos0,
+                                dense_max=dense_max, ids_cap=cap)
+        self.adesc = attn_desc(batch=batch, T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, ids_cap=cap,
+                               n_cells=N, scale=scale,
+                               q_dtype=QSA_F16 if q_f16 else QSA_F32,
+                               out_dtype=QSA_F16 if out_f16 else QSA_F32, strides=strides)
+        ws_bytes = qsa_index_topk_workspace(self.idesc)
+        n_part = qsa_partials_floats(self.adesc)
+        if ws_bytes == 0 or n_part == 0:
+            raise QsaError("unsupported or invalid workload shape")
+        self.ws = torch.empty(ws_bytes // 4, dtype=torch.int32, device=device)
+        self.ids = torch.empty((batch, T, cap), dtype=torch.int32, device=device)
+        self.n_sel = torch.empty((batch, T), dtype=torch.int32, device=device)
+        self.partials = torch.empty(n_part, dtype=torch.float32, device=device)
+        self.out = torch.empty((batch, T, Hq, D),
+                               dtype=torch.float16 if out_f16 else torch.float32,
+                               device=device)
+        rows = batch * T * Hq * P
+        self.pm = self.partials[:rows].view(batch, T, Hq, P)
+        self.pl = self.partials[rows:2 * rows].view(batch, T, Hq, P)
+        self.po = self.partials[2 * rows:].view(batch, T, Hq, P, D)
+
+    def index(self, q_idx, K_idx, stream=None):
+        qsa_index_topk(self.idesc, q_idx, K_idx, self.ids, self.n_sel, self.ws, stream)
+
+    def attend(self, q, Kq, Ksc, Vq, Vsc, stream=None, ids=None, n_sel=None):
+        qsa_attend(self.adesc, q, Kq, Ksc, Vq, Vsc, self.ids if ids is None else ids,
+                   self.n_sel if n_sel is None else n_sel, self.partials, stream)
+
+    def merge(self, stream=None):
+        qsa_merge(self.adesc, self.partials, self.out, stream)
+
+    def run(self, dev: dict, stream=None):
+        self.index(dev["q_idx"], dev["K_idx"], stream)
+        self.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"], stream)
+        self.merge(stream)
+        return self.out
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Copy the array fields of an input dict (numpy) to device tensors."""
+    out = {}
+    for key in ("q_idx", "K_idx", "q", "Kq", "Ksc", "Vq", "Vsc"):
+        out[key] = torch.from_numpy(inp[key]).to(device)
+    return out
+
+
+def path_for(inp: dict, *, P: int | None = None, device="cuda", strides=None) -> QsaPath:
+    """A QsaPath sized for an input dict produced by the seeded generator."""
+    return QsaPath(batch=inp["batch"], T=inp["T"], N=inp["N"], di=inp["di"], k=inp["k"],
+                   pos0=inp["pos0"], dense_max=inp["dense_max"], cap=inp["cap"],
+                   Hq=inp["Hq"], Hkv=inp["Hkv"], D=inp["D"],
+                   P=inp["P"] if P is None else P, q_f16=inp["q_dtype"] == "f16",
+                   out_f16=inp["out_dtype"] == "f16", device=device, strides=strides)
