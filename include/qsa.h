@@ -150,7 +150,8 @@ QSA_API int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const 
  * Supported: D in {64, 256}; Hq % Hkv == 0 with Hq/Hkv in {1,2,4,8,12,16};
  * 1 <= P <= 64; n_sel[t] <= ids_cap; all four cache base pointers and
  * batch strides 16-byte aligned; Kq/Vq cell strides multiples of 16;
- * Ksc/Vsc cell strides multiples of 4; 1 <= batch*T <= 2^31-1.
+ * Ksc/Vsc cell strides multiples of D/16 (the bytes of one head's scales);
+ * 1 <= batch*T <= 2^31-1.
  * --------------------------------------------------------------------- */
 typedef struct qsa_attn_desc {
     int batch;           /* B */

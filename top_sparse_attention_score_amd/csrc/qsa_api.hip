@@ -64,7 +64,8 @@ int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
     if (L->kq_cs < 0 || L->vq_cs < 0 || L->ksc_cs < 0 || L->vsc_cs < 0 || L->kq_bs < 0 ||
         L->vq_bs < 0 || L->ksc_bs < 0 || L->vsc_bs < 0)
         return QSA_ERR_INVALID_ARG;
-    if (L->kq_cs % 16 || L->vq_cs % 16 || L->ksc_cs % 4 || L->vsc_cs % 4)
+    const long long srow_g = d->D / 16;  // scale bytes of one head row
+    if (L->kq_cs % 16 || L->vq_cs % 16 || L->ksc_cs % srow_g || L->vsc_cs % srow_g)
         return QSA_ERR_INVALID_ARG;
     if (L->kq_bs % 16 || L->vq_bs % 16 || L->ksc_bs % 16 || L->vsc_bs % 16)
         return QSA_ERR_INVALID_ARG;

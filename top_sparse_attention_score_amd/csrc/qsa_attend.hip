@@ -10,8 +10,10 @@
 // share a KV head).  The merge rescales each chunk by exp(m_c - M), sums
 // l_c e_c and o_c e_c with fma in chunk order, then divides once.
 //
-// k_attend: one wave per (token, chunk, KV head); its G query heads share
-// every K and V row it gathers (GQA).  Cells are taken 64 at a time:
+// k_attend: one wave per (token, chunk, KV head), four chunks of the same
+// (token, KV head) per workgroup so they share the query rows in the scalar
+// cache; a wave's G query heads share every K and V row it gathers (GQA).
+// Cells are taken 64 at a time:
 //   QK  lane i owns cell i of the tile and streams that cell's int8 K row
 //       (D bytes) and fp16 scales; the G query rows are wave-uniform and are
 //       read from SGPRs (scalar loads), so each int8 code is converted once
@@ -28,6 +30,8 @@
 #include "qsa_launch.h"
 
 namespace qsa {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Loads N consecutive wave-uniform 32-bit words starting at element `off`.
 // The offset passes through an empty asm so the loads stay where they are
@@ -52,8 +56,46 @@ __device__ __forceinline__ half2_t int8_pair_to_half2(int w, int half_sel)
     return as_half2(bits) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
 }
 
+// Copies the V codes (D bytes) and V scales (D/16 bytes) of the tile's 64
+// cells from the cache straight into LDS (gfx950 global_load_lds, no VGPR
+// round trip).  Row-major: cell i's codes at v_s[i*D], scales at vsc_s[i*D/32].
+// `j` is this lane's cell (lane = cell); tail lanes hold a valid duplicate.
+template <int D>
+__device__ __forceinline__ void dma_v_tile(const char* Vb, long long vq_cs, const char* Vsb,
+                                           long long vsc_cs, int j, int8_t* v_s,
+                                           uint16_t* vsc_s)
+{
+    constexpr int LPC = D / 16;   // lanes per cell row (16 bytes each)
+    constexpr int CPI = 64 / LPC; // cells per instruction
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 64 / CPI; ++i) {
+        const int cell = i * CPI + lane / LPC;
+        const int jj = __shfl(j, cell, 64);
+        const char* src = Vb + (long long)jj * vq_cs + (lane % LPC) * 16;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(v_s + i * CPI * D), 16,
+                                         0, 0);
+    }
+    const char* ssrc = Vsb + (long long)j * vsc_cs;
+    if constexpr (D / 16 == 16)
+        __builtin_amdgcn_global_load_lds((const void*)ssrc, (lds_void_t*)vsc_s, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds((const void*)ssrc, (lds_void_t*)vsc_s, 4, 0, 0);
+}
+
+constexpr int kAttendWaves = 4;  // chunks of one (token, KV head) per workgroup
+
+// Orders this wave's LDS accesses: every earlier LDS access has completed and
+// all lanes of the wave have reached this point.  The waves of a workgroup
+// never share LDS, so no workgroup barrier is needed.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <int G, int D, bool QF16>
-__global__ __launch_bounds__(64) void k_attend(
+__global__ __launch_bounds__(64 * kAttendWaves) void k_attend(
     const void* __restrict__ q, const int8_t* __restrict__ Kq, const uint8_t* __restrict__ Ksc,
     const int8_t* __restrict__ Vq, const uint8_t* __restrict__ Vsc, long long kq_cs,
     long long ksc_cs, long long vq_cs, long long vsc_cs, long long kq_bs, long long ksc_bs,
@@ -64,11 +106,21 @@ __global__ __launch_bounds__(64) void k_attend(
     constexpr int NB = D / 32;        // scale blocks per head row
     constexpr int DPL = D / 64;       // output elements per lane
     constexpr int GP = (G + 3) & ~3;  // LDS row pitch of the tile weights
-    __shared__ float p_s[64 * GP];
+    constexpr int KC = D / 16;        // 16-byte chunks per K row
+    constexpr int SW = NB / 2;        // 32-bit words of scales per head row
+    __shared__ __align__(16) int8_t v_all[kAttendWaves][64 * D];
+    __shared__ __align__(16) uint16_t vsc_all[kAttendWaves][64 * NB];
+    __shared__ __align__(16) float p_all[kAttendWaves][64 * GP];
 
-    const int bt = blockIdx.x, c = blockIdx.y, g = blockIdx.z;
+    const int wave = threadIdx.x >> 6;
+    const int bt = blockIdx.x, c = blockIdx.y * kAttendWaves + wave, g = blockIdx.z;
+    if (c >= P)
+        return;
+    int8_t* v_s = v_all[wave];
+    uint16_t* vsc_s = vsc_all[wave];
+    float* p_s = p_all[wave];
     const int b = bt / T;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const size_t prow = (size_t)bt * Hq + (size_t)g * G;  // row of head g*G
 
     const int ns = min(n_sel[bt], cap);
@@ -106,58 +158,84 @@ __global__ __launch_bounds__(64) void k_attend(
             o[h][e] = 0.f;
     }
 
-#pragma unroll 1
-    for (int t0 = beg; t0 < end; t0 += 64) {
-        const int nt = min(64, end - t0);
-        const bool valid = lane < nt;
-        // Ids outside [0, N) are undefined input; clamping keeps every
-        // gather inside the cache.
-        const int j = min((unsigned)idr[t0 + (valid ? lane : 0)], (unsigned)(N - 1));
-
-        // ---- QK: lane = cell ------------------------------------------
-        const char* kr = Kb + (long long)j * kq_cs;
-        const uint32_t* ksr = (const uint32_t*)(Ksb + (long long)j * ksc_cs);
-        float ksc[NB];
+    // Lane = cell of the current 64-cell tile.  Ids outside [0, N) are
+    // undefined input; clamping keeps every gather inside the cache.  Tail
+    // lanes duplicate the tile's first cell so every load stays valid.
+    int t0 = beg;
+    int nt = min(64, end - t0);
+    int j = min((unsigned)idr[t0 + (lane < nt ? lane : 0)], (unsigned)(N - 1));
+    uint4 krow[KC];
+    uint32_t ksw[SW];
+    {
+        const uint4* kr = (const uint4*)(Kb + (long long)j * kq_cs);
 #pragma unroll
-        for (int w = 0; w < NB / 2; ++w) {
-            const uint32_t two = ksr[w];
-            ksc[2 * w] = half_bits_to_float((uint16_t)(two & 0xffffu));
-            ksc[2 * w + 1] = half_bits_to_float((uint16_t)(two >> 16));
-        }
+        for (int i = 0; i < KC; ++i)
+            krow[i] = kr[i];
+        const uint32_t* ks = (const uint32_t*)(Ksb + (long long)j * ksc_cs);
+#pragma unroll
+        for (int w = 0; w < SW; ++w)
+            ksw[w] = ks[w];
+    }
+
+#pragma unroll 1
+    for (;;) {
+        const bool valid = lane < nt;
+        const int t1 = t0 + 64;
+        const bool more = t1 < end;
+        const int nt1 = more ? min(64, end - t1) : 0;
+        int jn = 0;
+        // Settle the K row (loaded during the previous PV phase) before any
+        // copy of this tile is issued: after this no K use waits on memory,
+        // so the V copy below overlaps the whole QK phase.
+#pragma unroll
+        for (int i = 0; i < KC; ++i)
+            asm volatile("" : "+v"(krow[i].x), "+v"(krow[i].y), "+v"(krow[i].z),
+                         "+v"(krow[i].w));
+#pragma unroll
+        for (int w = 0; w < SW; ++w)
+            asm volatile("" : "+v"(ksw[w]));
+        dma_v_tile<D>(Vb, vq_cs, Vsb, vsc_cs, j, v_s, vsc_s);
+        if (more)
+            jn = idr[t1 + (lane < nt1 ? lane : 0)];
+
+        // ---- QK: lane = cell, K row in VGPRs, queries in SGPRs --------
+        // The query row offset is re-derived each tile (empty asm) so the
+        // per-segment offsets below are computed inside the loop instead of
+        // being precomputed and held for every segment.
+        size_t qrow = prow * D;
+        asm volatile("" : "+s"(qrow));
         float x[G];
 #pragma unroll
         for (int h = 0; h < G; ++h)
             x[h] = 0.f;
-        // The G x D query values are wave-uniform and are scalar-loaded one
-        // head (32 values of one scale block) ahead of use; sched_barrier
-        // fences keep the compiler from hoisting all of them at once, which
-        // would overflow the SGPR file.
-        int4 wa0 = *(const int4*)(kr);
-        int4 wa1 = *(const int4*)(kr + 16);
-#pragma unroll 1
+#pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
-            const int nblk = min(blk + 1, NB - 1);
-            const int4 wb0 = *(const int4*)(kr + nblk * 32);  // next block's codes
-            const int4 wb1 = *(const int4*)(kr + nblk * 32 + 16);
-            const int ww[8] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w};
+            const uint4 w0 = krow[2 * blk], w1 = krow[2 * blk + 1];
+            const int ww[8] = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
+                               (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+            const uint32_t sw = ksw[blk / 2];
+            const float ksc = half_bits_to_float((uint16_t)((blk & 1) ? (sw >> 16) : (sw & 0xffffu)));
+
             if constexpr (!QF16) {
                 float kf[32];
 #pragma unroll
                 for (int e = 0; e < 32; ++e)
                     kf[e] = sbyte_to_float(ww[e >> 2], e & 3);
+                // One head's 32 query values of this block at a time; the next
+                // head's are scalar-loaded while these are used.
                 const float* qf = (const float*)q;
                 float qc[32], qn[32];
-                load_uniform<32>(qf, prow * D + blk * 32, qc);
+                load_uniform<32>(qf, qrow + blk * 32, qc);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     if (h + 1 < G)
-                        load_uniform<32>(qf, (prow + h + 1) * D + blk * 32, qn);
+                        load_uniform<32>(qf, qrow + (h + 1) * D + blk * 32, qn);
                     __builtin_amdgcn_sched_barrier(0);
                     float part = 0.f;
 #pragma unroll
                     for (int e = 0; e < 32; ++e)
                         part = fmaf(qc[e], kf[e], part);
-                    x[h] = fmaf(ksc[blk], part, x[h]);
+                    x[h] = fmaf(ksc, part, x[h]);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int e = 0; e < 32; ++e)
@@ -175,25 +253,23 @@ __global__ __launch_bounds__(64) void k_attend(
                 }
                 const uint32_t* q2 = (const uint32_t*)q;
                 uint32_t qc[16], qn[16];
-                load_uniform<16>(q2, (prow * D + blk * 32) / 2, qc);
+                load_uniform<16>(q2, (qrow + blk * 32) / 2, qc);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     if (h + 1 < G)
-                        load_uniform<16>(q2, ((prow + h + 1) * D + blk * 32) / 2, qn);
+                        load_uniform<16>(q2, (qrow + (h + 1) * D + blk * 32) / 2, qn);
                     __builtin_amdgcn_sched_barrier(0);
                     float part = 0.f;
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
                         part = __builtin_amdgcn_fdot2(as_half2(qc[e]), k2[e], part, false);
-                    x[h] = fmaf(ksc[blk], part, x[h]);
+                    x[h] = fmaf(ksc, part, x[h]);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
                         qc[e] = qn[e];
                 }
             }
-            wa0 = wb0;
-            wa1 = wb1;
         }
 
         // ---- softmax over the tile, folded into the running pair -------
@@ -210,28 +286,41 @@ __global__ __launch_bounds__(64) void k_attend(
             m_run[h] = mn;
             p_s[lane * GP + h] = p;
         }
-        __syncthreads();
 
-        // ---- PV: lane = DPL output elements, loop over the tile's cells --
+        // ---- V copy complete; next tile's K rows in flight during PV ----
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("" : "+v"(jn));   // keep the use of the prefetched ids here
+        int j1 = j;
+        if (more) {
+            j1 = min((unsigned)jn, (unsigned)(N - 1));
+            const uint4* kr = (const uint4*)(Kb + (long long)j1 * kq_cs);
+#pragma unroll
+            for (int i = 0; i < KC; ++i)
+                krow[i] = kr[i];
+            const uint32_t* ks = (const uint32_t*)(Ksb + (long long)j1 * ksc_cs);
+#pragma unroll
+            for (int w = 0; w < SW; ++w)
+                ksw[w] = ks[w];
+        }
+        wave_lds_sync();   // p_s written; V tile landed in LDS
+
+        // ---- PV: lane = DPL output elements, cells from LDS -------------
         const int dsc = (lane * DPL) >> 5;  // scale block of this lane's elements
 #pragma unroll 4
         for (int i = 0; i < nt; ++i) {
-            const int jj = __builtin_amdgcn_readlane(j, i);
-            const char* vr = Vb + (long long)jj * vq_cs + lane * DPL;
-            const float vs = half_bits_to_float(
-                *(const uint16_t*)(Vsb + (long long)jj * vsc_cs + dsc * 2));
+            const float vs = half_bits_to_float(vsc_s[i * NB + dsc]);
             float vf[DPL];
             if constexpr (DPL == 4) {
-                const int w = *(const int*)vr;
+                const int w = *(const int*)(v_s + i * D + lane * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     vf[e] = sbyte_to_float(w, e) * vs;
             } else if constexpr (DPL == 2) {
-                const int w = (int)*(const uint16_t*)vr;
+                const int w = (int)*(const uint16_t*)(v_s + i * D + lane * 2);
                 vf[0] = sbyte_to_float(w, 0) * vs;
                 vf[1] = sbyte_to_float(w, 1) * vs;
             } else {
-                vf[0] = (float)(*(const int8_t*)vr) * vs;
+                vf[0] = (float)v_s[i * D + lane] * vs;
             }
             const float* pr = p_s + i * GP;
 #pragma unroll
@@ -242,7 +331,12 @@ __global__ __launch_bounds__(64) void k_attend(
                     o[h][e] = fmaf(pv, vf[e], o[h][e]);
             }
         }
-        __syncthreads();
+        wave_lds_sync();   // LDS reads done before the next tile's copies
+        if (!more)
+            break;
+        t0 = t1;
+        nt = nt1;
+        j = j1;
     }
 
 #pragma unroll
@@ -301,15 +395,16 @@ __global__ __launch_bounds__(D) void k_merge(const float* __restrict__ pm,
 template <int G, int D>
 static void launch_attend_gd(const AttnLaunch& a, hipStream_t s)
 {
-    dim3 grid((unsigned)(a.B * a.T), (unsigned)a.P, (unsigned)a.Hkv);
+    dim3 grid((unsigned)(a.B * a.T), (unsigned)((a.P + kAttendWaves - 1) / kAttendWaves),
+              (unsigned)a.Hkv);
 #define QSA_ATTEND_ARGS                                                                      \
     a.q, a.Kq, (const uint8_t*)a.Ksc, a.Vq, (const uint8_t*)a.Vsc, a.kq_cs, a.ksc_cs, a.vq_cs, \
         a.vsc_cs, a.kq_bs, a.ksc_bs, a.vq_bs, a.vsc_bs, a.ids, a.n_sel, a.pm, a.pl, a.po, a.T, \
         a.Hq, a.P, a.cap, a.N, a.scale
     if (a.q_f16)
-        k_attend<G, D, true><<<grid, 64, 0, s>>>(QSA_ATTEND_ARGS);
+        k_attend<G, D, true><<<grid, 64 * kAttendWaves, 0, s>>>(QSA_ATTEND_ARGS);
     else
-        k_attend<G, D, false><<<grid, 64, 0, s>>>(QSA_ATTEND_ARGS);
+        k_attend<G, D, false><<<grid, 64 * kAttendWaves, 0, s>>>(QSA_ATTEND_ARGS);
 #undef QSA_ATTEND_ARGS
 }
 

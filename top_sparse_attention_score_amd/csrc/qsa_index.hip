@@ -9,10 +9,10 @@
 // Layer-Local Aliasing", section 1, Target 2).
 //
 // Kernels
-//   k_idx_scan   decode (T <= 16): one thread per cell streams the cell's fp16
-//                key row once and scores it against all T tokens with
-//                v_dot2 (fp16 x fp16 products, fp32 accumulation); the T
-//                index queries are wave-uniform and live in SGPRs.
+//   k_idx_scan   decode (T <= 16): streams every visible cell's fp16 key row
+//                once, 16 lanes per row (coalesced), scores it against all T
+//                tokens with v_dot2 (fp16 x fp16 products, fp32
+//                accumulation) and sums the row across its lanes with DPP.
 //   k_idx_gemm   prompt chunk (T > 16): [T x d_idx] x [d_idx x N] on MFMA
 //                (v_mfma_f32_16x16x16_f16), 64 tokens x 64 cells per
 //                workgroup.
@@ -28,43 +28,76 @@ namespace qsa {
 
 // ---------------------------------------------------------------- scan ---
 
+// Sum over the LPR lanes that share a key row (LPR = 16 or 8 consecutive
+// lanes).  16 lanes: DPP row rotations (every lane ends with the total);
+// 8 lanes: butterfly shuffles.  Partial sums of grid-valued products are
+// exact, so the order does not change the result.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v)
+{
+    if constexpr (LPR == 16) {
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+    } else {
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1)
+            v += __shfl_xor(v, o, LPR);
+    }
+    return v;
+}
+
+// One key row (DI fp16 = DI*2 bytes) is read by LPR = DI/8 consecutive lanes,
+// 16 bytes each, so every load instruction of a wave covers 64/LPR whole,
+// consecutive rows: fully coalesced.  Each lane keeps the 8 index-query
+// values of its slice for all T tokens in registers.
 template <int DI, int TT>
-__global__ __launch_bounds__(256) void k_idx_scan(const uint32_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256) void k_idx_scan(const uint4* __restrict__ q_idx,
                                                   const uint4* __restrict__ K_idx,
                                                   uint32_t* __restrict__ keys, int T, int N,
                                                   int nvis_max)
 {
+    constexpr int LPR = DI / 8;           // lanes per row
+    constexpr int RPI = 256 / LPR;        // rows per block-wide step
+    constexpr int U = 8;                  // steps in flight per thread
     const int b = blockIdx.y;
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= nvis_max)
-        return;
-    const uint4* row = K_idx + ((size_t)b * N + j) * (DI / 8);
-    const uint32_t* qb = q_idx + (size_t)b * T * (DI / 2);
-    uint4 kv[DI / 8];
-#pragma unroll
-    for (int c = 0; c < DI / 8; ++c)
-        kv[c] = row[c];
-    float acc[TT];
+    const int sub = threadIdx.x % LPR;
+    const int r0 = blockIdx.x * (RPI * U) + threadIdx.x / LPR;
+
+    uint4 qv[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t)
-        acc[t] = 0.f;
+        qv[t] = (t < T) ? q_idx[((size_t)b * T + t) * (DI / 8) + sub] : make_uint4(0, 0, 0, 0);
+
+    uint4 kv[U];
 #pragma unroll
-    for (int c = 0; c < DI / 8; ++c) {
-        const uint32_t kw[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
+    for (int u = 0; u < U; ++u) {
+        const int j = min(r0 + u * RPI, nvis_max - 1);
+        kv[u] = K_idx[((size_t)b * N + j) * (DI / 8) + sub];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = r0 + u * RPI;
+        const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
             if (t < T) {
+                const uint32_t qw[4] = {qv[t].x, qv[t].y, qv[t].z, qv[t].w};
+                float acc = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[t] = __builtin_amdgcn_fdot2(as_half2(qb[t * (DI / 2) + c * 4 + e]),
-                                                    as_half2(kw[e]), acc[t], false);
+                    acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
+                acc = row_sum<LPR>(acc);
+                if (sub == 0 && j < nvis_max)
+                    keys[((size_t)b * T + t) * N + j] = score_key(acc);
             }
         }
     }
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-        if (t < T)
-            keys[((size_t)b * T + t) * N + j] = score_key(acc[t]);
 }
 
 // ---------------------------------------------------------------- gemm ---
@@ -283,8 +316,9 @@ size_t index_workspace_bytes(int B, int T, int N)
 template <int DI>
 static void launch_scan(const IndexLaunch& a, int nvis_max, hipStream_t s)
 {
-    dim3 grid((nvis_max + 255) / 256, a.B);
-    const uint32_t* q = (const uint32_t*)a.q_idx;
+    constexpr int rows_per_block = (256 / (DI / 8)) * 8;
+    dim3 grid((nvis_max + rows_per_block - 1) / rows_per_block, a.B);
+    const uint4* q = (const uint4*)a.q_idx;
     const uint4* K = (const uint4*)a.K_idx;
     if (a.T <= 1)
         k_idx_scan<DI, 1><<<grid, 256, 0, s>>>(q, K, a.keys, a.T, a.N, nvis_max);
