@@ -103,6 +103,9 @@ def main() -> None:
                     help="distinct seeded problems, tiled to the batch on the GPU")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB "
+                         "(a known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -130,6 +133,14 @@ def main() -> None:
     inp = dict(base)
     inp["batch"] = B
     path = qsa.path_for(inp, P=P)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 18        # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()

@@ -96,7 +96,7 @@ QSA_API int qsa_version(void);
  * 1024) this is the exact-arithmetic selection.
  *
  * Supported: d_idx in {64, 128}; 1 <= k <= ids_cap; 0 <= dense_max <=
- * ids_cap; 0 <= pos0; pos0 + T <= N; 1 <= batch <= 65535.
+ * ids_cap; 0 <= pos0; pos0 + T <= N <= 2^22; 1 <= batch*T <= 65535.
  * --------------------------------------------------------------------- */
 typedef struct qsa_index_desc {
     int batch;      /* B */
@@ -151,7 +151,7 @@ QSA_API int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const 
  * 1 <= P <= 64; n_sel[t] <= ids_cap; all four cache base pointers and
  * batch strides 16-byte aligned; Kq/Vq cell strides multiples of 16;
  * Ksc/Vsc cell strides multiples of D/16 (the bytes of one head's scales);
- * 1 <= batch*T <= 2^31-1.
+ * batch*T*Hq*P <= 2^31-1.
  * --------------------------------------------------------------------- */
 typedef struct qsa_attn_desc {
     int batch;           /* B */

@@ -102,7 +102,7 @@ def test_index_desc_rejected(kw, code):
 def test_index_pointer_and_workspace_checks():
     d = _idesc()
     need = qb.lib().qsa_index_topk_workspace(ctypes.byref(d))
-    assert need == 8192 * 4
+    assert need >= 8192 * 4          # at least one score key per visible cell
     L = qb.lib()
     assert L.qsa_index_topk(ctypes.byref(d), None, 16, 16, 16, 16, need, None) == INVALID
     assert L.qsa_index_topk(ctypes.byref(d), 8, 16, 16, 16, 16, need, None) == INVALID

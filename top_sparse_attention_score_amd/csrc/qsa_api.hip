@@ -25,7 +25,9 @@ int check_index(const qsa_index_desc* d)
         return QSA_ERR_INVALID_ARG;
     if (d->d_idx != 64 && d->d_idx != 128)
         return QSA_ERR_UNSUPPORTED;
-    if (d->batch > 65535 || (long long)d->batch * d->T > INT_MAX)
+    if (d->batch > 65535 || (long long)d->batch * d->T > 65535)
+        return QSA_ERR_UNSUPPORTED;
+    if (d->n_cells > qsa::index_max_cells() || (long long)d->ids_cap > INT_MAX / 2)
         return QSA_ERR_UNSUPPORTED;
     return QSA_OK;
 }
@@ -48,7 +50,7 @@ int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
     if (!qsa::attend_supported(d->Hq / d->Hkv, d->D))
         return QSA_ERR_UNSUPPORTED;
     const long long bt = (long long)d->batch * d->T;
-    if (bt > INT_MAX || bt * d->Hq > INT_MAX || d->Hkv > 65535)
+    if (bt * d->P > INT_MAX || bt * d->Hq * d->P > INT_MAX || d->Hkv > 65535)
         return QSA_ERR_UNSUPPORTED;
 
     const long long row = (long long)d->Hkv * d->D;           // int8 codes per cell
@@ -140,7 +142,7 @@ int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const void* K_
     a.K_idx = K_idx;
     a.ids = ids;
     a.n_sel = n_sel;
-    a.keys = (uint32_t*)ws;
+    a.ws = ws;
     if (qsa::launch_index_topk(a, (hipStream_t)stream) != hipSuccess)
         return QSA_ERR_HIP;
     return QSA_OK;

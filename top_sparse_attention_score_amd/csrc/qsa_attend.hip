@@ -10,9 +10,10 @@
 // share a KV head).  The merge rescales each chunk by exp(m_c - M), sums
 // l_c e_c and o_c e_c with fma in chunk order, then divides once.
 //
-// k_attend: one wave per (token, chunk, KV head), four chunks of the same
-// (token, KV head) per workgroup so they share the query rows in the scalar
-// cache; a wave's G query heads share every K and V row it gathers (GQA).
+// k_attend: one wave per (token, chunk, KV head), four consecutive (token,
+// chunk) items per workgroup, so chunks of one token share its query rows in
+// the scalar cache; a wave's G query heads share every K and V row it
+// gathers (GQA).
 // Cells are taken 64 at a time:
 //   QK  lane i owns cell i of the tile and streams that cell's int8 K row
 //       (D bytes) and fp16 scales; the G query rows are wave-uniform and are
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(64 * kAttendWaves) void k_attend(
     long long ksc_cs, long long vq_cs, long long vsc_cs, long long kq_bs, long long ksc_bs,
     long long vq_bs, long long vsc_bs, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ n_sel, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ po, int T, int Hq, int P, int cap, int N, float scale)
+    float* __restrict__ po, int T, int Hq, int P, int cap, int N, int BT, float scale)
 {
     constexpr int NB = D / 32;        // scale blocks per head row
     constexpr int DPL = D / 64;       // output elements per lane
@@ -112,10 +113,14 @@ __global__ __launch_bounds__(64 * kAttendWaves) void k_attend(
     __shared__ __align__(16) uint16_t vsc_all[kAttendWaves][64 * NB];
     __shared__ __align__(16) float p_all[kAttendWaves][64 * GP];
 
-    const int wave = threadIdx.x >> 6;
-    const int bt = blockIdx.x, c = blockIdx.y * kAttendWaves + wave, g = blockIdx.z;
-    if (c >= P)
+    // Each wave takes one (token, chunk) item; consecutive items are the
+    // chunks of one token, so for P >= 4 the waves of a workgroup share the
+    // token's query rows, and for small P no wave of a workgroup idles.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const long long item = (long long)blockIdx.x * kAttendWaves + wave;
+    if (item >= (long long)BT * P)
         return;
+    const int bt = (int)(item / P), c = (int)(item % P), g = blockIdx.y;
     int8_t* v_s = v_all[wave];
     uint16_t* vsc_s = vsc_all[wave];
     float* p_s = p_all[wave];
@@ -395,12 +400,12 @@ __global__ __launch_bounds__(D) void k_merge(const float* __restrict__ pm,
 template <int G, int D>
 static void launch_attend_gd(const AttnLaunch& a, hipStream_t s)
 {
-    dim3 grid((unsigned)(a.B * a.T), (unsigned)((a.P + kAttendWaves - 1) / kAttendWaves),
-              (unsigned)a.Hkv);
+    const long long items = (long long)a.B * a.T * a.P;
+    dim3 grid((unsigned)((items + kAttendWaves - 1) / kAttendWaves), (unsigned)a.Hkv);
 #define QSA_ATTEND_ARGS                                                                      \
     a.q, a.Kq, (const uint8_t*)a.Ksc, a.Vq, (const uint8_t*)a.Vsc, a.kq_cs, a.ksc_cs, a.vq_cs, \
         a.vsc_cs, a.kq_bs, a.ksc_bs, a.vq_bs, a.vsc_bs, a.ids, a.n_sel, a.pm, a.pl, a.po, a.T, \
-        a.Hq, a.P, a.cap, a.N, a.scale
+        a.Hq, a.P, a.cap, a.N, a.B * a.T, a.scale
     if (a.q_f16)
         k_attend<G, D, true><<<grid, 64 * kAttendWaves, 0, s>>>(QSA_ATTEND_ARGS);
     else

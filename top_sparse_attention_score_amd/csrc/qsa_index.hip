@@ -16,11 +16,10 @@
 //   k_idx_gemm   prompt chunk (T > 16): [T x d_idx] x [d_idx x N] on MFMA
 //                (v_mfma_f32_16x16x16_f16), 64 tokens x 64 cells per
 //                workgroup.
-//   k_select_row one 1024-thread workgroup per token: 3-digit radix select
-//                (11/11/10 bits) of the k-th largest key in LDS histograms,
-//                then an ordered compaction that writes the kept ids in
-//                ascending cell order, giving the tie quota at the threshold
-//                to the lowest cell indices.
+//   k_sel_*      exact top-k over the score keys, tiled over the whole chip
+//                (histogram, filter + pivot, ordered write); see below.
+#include <algorithm>
+
 #include "qsa_device.h"
 #include "qsa_launch.h"
 
@@ -168,11 +167,51 @@ __global__ __launch_bounds__(256) void k_idx_gemm(const _Float16* __restrict__ q
 }
 
 // -------------------------------------------------------------- select ---
+//
+// Exact top-k over the fp32 score keys of one token, spread over the whole
+// chip.  Keys are order-preserving uint32 images of the scores; the kept set
+// is every cell that is not below the pivot, the k-th cell in the total order
+// (key descending, cell index ascending), so ties at the threshold go to the
+// lowest indices.  A token is cut into tiles of kTile cells:
+//   k_sel_hist    per tile: LDS histogram of the top 11 key bits, merged into
+//                 the token's 2048-bin histogram with global atomics;
+//   k_sel_filter  per tile: from that histogram the bin holding the k-th key;
+//                 counts the tile's cells above that bin (all kept) and
+//                 appends the cells inside it to the token's candidate list;
+//   k_sel_pivot   per token: resolves the pivot with two more radix digits
+//                 on the key, then on the cell index among equal keys, and
+//                 turns the per-tile kept counts into output offsets;
+//   k_sel_write   per tile: ordered compaction of the kept cells to their
+//                 offsets, so ids come out in ascending cell order.
+// Tokens that see at most max(dense_max, k) cells keep all of them.  If the
+// threshold bin holds more than kCap candidates (massive exact ties), the
+// pivot kernel streams the token's keys instead.  Kernel boundaries order the
+// steps; no workgroup waits on another.
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 256;
+constexpr int kTile = 4096;                         // cells per select tile
+constexpr int kPerLane = kTile / kSelThreads;       // 16 keys per thread
+constexpr int kBins = 2048;
+constexpr int kCap = 4096;                          // candidates per token
+constexpr int kMaxTiles = 1024;                     // n_cells <= 2^22
 
-// Exclusive prefix sum over the 1024 threads of the block; `total` receives
-// the block sum.  s_wave holds 16 words of LDS.
+struct SelWs {
+    uint32_t* keys;      // [BT][N]
+    uint32_t* hist;      // [BT][kBins]
+    uint32_t* tile_def;  // [BT][NT] cells above the threshold bin, per tile
+    uint32_t* tile_off;  // [BT][NT] output offset of each tile
+    uint32_t* cand_n;    // [BT] candidates appended
+    uint32_t* done;      // [BT] finished filter tiles
+    uint32_t* cand;      // [BT][kCap][2] (key, cell)
+    uint32_t* pivot;     // [BT][2] (key, cell index) of the k-th kept cell
+};
+
+__host__ __device__ __forceinline__ bool token_selects(int nvis, int k, int dense_max)
+{
+    return nvis > dense_max && nvis > k;
+}
+
+// Exclusive prefix sum over the 256 threads; `total` gets the block sum.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total,
                                                     uint32_t* s_wave)
 {
@@ -199,167 +238,475 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total,
     return base + x - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select_row(const uint32_t* __restrict__ keys,
-                                                            int32_t* __restrict__ ids,
-                                                            int32_t* __restrict__ n_sel, int T,
-                                                            int N, int pos0, int k,
-                                                            int dense_max, int cap)
+// Given a histogram of nb bins (LDS), finds the bin b holding the r-th
+// largest element (1-based) and the count of elements in higher bins.
+// Every thread gets the result.
+__device__ __forceinline__ void find_bin_desc(const uint32_t* hist, int nb, uint32_t r,
+                                              uint32_t& bin, uint32_t& above,
+                                              uint32_t* s_wave, uint32_t* s_pick)
 {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t s_wave[kSelThreads / 64];
-    __shared__ uint32_t s_pick[2];
-    if (threadIdx.x == 0) {
-        s_pick[0] = 0u;
-        s_pick[1] = 0u;
+    const int per = nb / kSelThreads;  // bins per thread (8 or 4)
+    const int hi = nb - 1 - threadIdx.x * per;  // thread's bins: hi, hi-1, ...
+    uint32_t sum = 0;
+    for (int i = 0; i < per; ++i)
+        sum += hist[hi - i];
+    uint32_t total;
+    const uint32_t ex = block_excl_scan(sum, total, s_wave);
+    if (ex < r && r <= ex + sum) {
+        uint32_t acc = ex;
+        for (int i = 0; i < per; ++i) {
+            const uint32_t c = hist[hi - i];
+            if (acc < r && r <= acc + c) {
+                s_pick[0] = (uint32_t)(hi - i);
+                s_pick[1] = acc;
+            }
+            acc += c;
+        }
     }
+    __syncthreads();
+    bin = s_pick[0];
+    above = s_pick[1];
+    __syncthreads();
+}
 
-    const int bt = blockIdx.x;
-    const int t = bt % T;
-    const int nvis = pos0 + t + 1;
-    const int tid = threadIdx.x;
-    int32_t* row = ids + (size_t)bt * cap;
-
-    if (nvis <= dense_max || nvis <= k) {
-        // Dense fallback, or no more visible cells than k: keep them all.
-        for (int i = tid; i < cap; i += kSelThreads)
-            row[i] = (i < nvis) ? i : -1;
-        if (tid == 0)
-            n_sel[bt] = nvis;
-        return;
-    }
-
-    const uint32_t* kr = keys + (size_t)bt * N;
-    uint32_t prefix = 0u, pmask = 0u;
-    uint32_t need = (uint32_t)k;  // rank (from the top) still to locate
-
-    // Radix select over the 32-bit key: digits of 11, 11 and 10 bits.
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = (pass == 0) ? 21 : (pass == 1) ? 10 : 0;
-        const int nb = (pass == 2) ? 1024 : 2048;
-        for (int i = tid; i < nb; i += kSelThreads)
+// Radix select: among the values produced by get(i, v) for i < n (get returns
+// false to skip), whose bits under pmask equal prefix, finds the r-th largest.
+// Digits (11, 11, 10 bits) from digit `first` on.  On return prefix is the
+// value and r the number of elements equal to it still to take.
+template <class Get>
+__device__ void radix_kth_largest(int n, Get get, int first, uint32_t& prefix,
+                                  uint32_t& pmask, uint32_t& r, uint32_t* hist,
+                                  uint32_t* s_wave, uint32_t* s_pick)
+{
+    for (int d = first; d < 3; ++d) {
+        const int shift = (d == 0) ? 21 : (d == 1) ? 10 : 0;
+        const int nb = (d == 2) ? 1024 : 2048;
+        for (int i = threadIdx.x; i < nb; i += kSelThreads)
             hist[i] = 0u;
         __syncthreads();
-        for (int j = tid; j < nvis; j += kSelThreads) {
-            const uint32_t u = kr[j];
-            if ((u & pmask) == prefix)
-                atomicAdd(&hist[(u >> shift) & (uint32_t)(nb - 1)], 1u);
+        for (int i = threadIdx.x; i < n; i += kSelThreads) {
+            uint32_t v;
+            if (get(i, v) && (v & pmask) == prefix)
+                atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        // Walk bins from the top: thread tid owns the bins at descending
-        // positions 2*tid, 2*tid+1 (2048 bins) or tid (1024 bins).
-        uint32_t c_hi, c_lo;
-        int b_hi;
-        if (nb == 2048) {
-            b_hi = nb - 1 - 2 * tid;
-            c_hi = hist[b_hi];
-            c_lo = hist[b_hi - 1];
-        } else {
-            b_hi = nb - 1 - tid;
-            c_hi = hist[b_hi];
-            c_lo = 0u;
-        }
-        uint32_t total;
-        const uint32_t above = block_excl_scan(c_hi + c_lo, total, s_wave);
-        if (above < need && need <= above + c_hi) {
-            s_pick[0] = (uint32_t)b_hi;
-            s_pick[1] = above;
-        } else if (nb == 2048 && above + c_hi < need && need <= above + c_hi + c_lo) {
-            s_pick[0] = (uint32_t)(b_hi - 1);
-            s_pick[1] = above + c_hi;
-        }
-        __syncthreads();
-        const uint32_t bin = s_pick[0];
-        need -= s_pick[1];
+        uint32_t bin, above;
+        find_bin_desc(hist, nb, r, bin, above, s_wave, s_pick);
+        r -= above;
         prefix |= bin << shift;
         pmask |= (uint32_t)(nb - 1) << shift;
-        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_sel_clear(SelWs w, int BT)
+{
+    const size_t n = (size_t)BT * kBins;
+    for (size_t i = (size_t)blockIdx.x * kSelThreads + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * kSelThreads)
+        w.hist[i] = 0u;
+    for (size_t i = (size_t)blockIdx.x * kSelThreads + threadIdx.x; i < (size_t)BT;
+         i += (size_t)gridDim.x * kSelThreads) {
+        w.cand_n[i] = 0u;
+        w.done[i] = 0u;
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_sel_hist(SelWs w, int T, int N, int pos0,
+                                                          int k, int dense_max)
+{
+    __shared__ uint32_t hist[kBins];
+    const int bt = blockIdx.y;
+    const int nvis = pos0 + (bt % T) + 1;
+    const int j0 = blockIdx.x * kTile;
+    if (!token_selects(nvis, k, dense_max) || j0 >= nvis)
+        return;
+    for (int i = threadIdx.x; i < kBins; i += kSelThreads)
+        hist[i] = 0u;
+    __syncthreads();
+    const uint32_t* kr = w.keys + (size_t)bt * N;
+    const int j1 = min(j0 + kTile, nvis);
+    uint32_t u[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int j = j0 + i * kSelThreads + (int)threadIdx.x;
+        u[i] = (j < j1) ? kr[j] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i)
+        if (j0 + i * kSelThreads + (int)threadIdx.x < j1)
+            atomicAdd(&hist[u[i] >> 21], 1u);
+    __syncthreads();
+    uint32_t* gh = w.hist + (size_t)bt * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kSelThreads) {
+        const uint32_t c = hist[i];
+        if (c)
+            atomicAdd(&gh[i], c);
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_sel_filter(SelWs w, int T, int N, int NT,
+                                                            int pos0, int k, int dense_max)
+{
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t s_wave[kSelThreads / 64];
+    __shared__ uint32_t s_pick[2];
+
+    const int bt = blockIdx.y;
+    const int nvis = pos0 + (bt % T) + 1;
+    const int tile = blockIdx.x;
+    const int j0 = tile * kTile;
+    if (!token_selects(nvis, k, dense_max) || j0 >= nvis)
+        return;
+    const uint32_t* kr = w.keys + (size_t)bt * N;
+
+    // Bin of the k-th largest key, and how many keys lie above that bin.
+    const uint32_t* gh = w.hist + (size_t)bt * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kSelThreads)
+        hist[i] = gh[i];
+    __syncthreads();
+    uint32_t b1, above1;
+    find_bin_desc(hist, kBins, (uint32_t)k, b1, above1, s_wave, s_pick);
+
+    // This tile: count keys above the bin, append keys inside it.  Each wave
+    // owns a contiguous quarter of the tile, loads it 64 keys per step with
+    // all loads in flight at once, counts with ballots; one atomic per
+    // workgroup reserves candidate slots, then the candidates are written.
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int j1 = min(j0 + kTile, nvis);
+    const int wb = j0 + wv * (kTile / 4);
+    uint32_t u[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int j = wb + i * 64 + lane;
+        u[i] = (j < j1) ? kr[j] : 0u;
+    }
+    uint32_t n_def = 0, n_cand = 0;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const bool ok = wb + i * 64 + lane < j1;
+        const uint32_t bin = u[i] >> 21;
+        n_def += (uint32_t)__popcll(__ballot(ok && bin > b1));
+        n_cand += (uint32_t)__popcll(__ballot(ok && bin == b1));
+    }
+    __shared__ uint32_t s_nc[kSelThreads / 64], s_nd[kSelThreads / 64], s_base;
+    if (lane == 0) {
+        s_nc[wv] = n_cand;
+        s_nd[wv] = n_def;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t tc = 0, td = 0;
+        for (int i = 0; i < kSelThreads / 64; ++i) {
+            tc += s_nc[i];
+            td += s_nd[i];
+        }
+        s_base = tc ? atomicAdd(&w.cand_n[bt], tc) : 0u;
+        w.tile_def[(size_t)bt * NT + tile] = td;
+    }
+    __syncthreads();
+    uint32_t* cand = w.cand + (size_t)bt * kCap * 2;
+    uint32_t slot = s_base;
+    for (int i = 0; i < wv; ++i)
+        slot += s_nc[i];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int j = wb + i * 64 + lane;
+        const bool is_c = j < j1 && (u[i] >> 21) == b1;
+        const unsigned long long m = __ballot(is_c);
+        const uint32_t pos = slot + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (is_c && pos < (uint32_t)kCap) {
+            cand[2 * pos] = u[i];
+            cand[2 * pos + 1] = (uint32_t)j;
+        }
+        slot += (uint32_t)__popcll(m);
     }
 
-    // prefix is now the key of the k-th kept cell; `need` of the cells with
-    // exactly that key are kept, lowest indices first.  Ordered compaction.
-    const uint32_t tau = prefix;
-    uint32_t run_gt = 0u, run_eq = 0u;
-#pragma unroll 1
-    for (int base = 0; base < nvis; base += kSelThreads) {
-        const int j = base + tid;
-        const uint32_t u = (j < nvis) ? kr[j] : 0u;
-        const uint32_t gt = (u > tau) ? 1u : 0u;
-        const uint32_t eq = (u == tau) ? 1u : 0u;
-        uint32_t total;
-        const uint32_t ex = block_excl_scan(gt | (eq << 16), total, s_wave);
-        const uint32_t gt_ex = ex & 0xffffu, eq_ex = ex >> 16;
-        const uint32_t eq_before = run_eq + eq_ex;
-        if (gt || (eq && eq_before < need)) {
-            const uint32_t pos = run_gt + gt_ex + min(eq_before, need);
-            if (pos < (uint32_t)k)
-                row[pos] = j;
+}
+
+// One workgroup per selecting token: from the per-tile counts and the
+// candidate list, the exact pivot (key, cell) of the k-th kept cell, and the
+// output offset of every tile.
+__global__ __launch_bounds__(kSelThreads) void k_sel_pivot(SelWs w, int32_t* __restrict__ n_sel,
+                                                           int T, int N, int NT, int pos0,
+                                                           int k, int dense_max)
+{
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t s_wave[kSelThreads / 64];
+    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t c_key[kCap];
+    __shared__ uint32_t c_idx[kCap];
+    __shared__ uint32_t s_tile[kMaxTiles];
+
+    const int bt = blockIdx.x;
+    const int nvis = pos0 + (bt % T) + 1;
+    if (!token_selects(nvis, k, dense_max))
+        return;
+    const int nt_eff = (nvis + kTile - 1) / kTile;
+    const uint32_t* kr = w.keys + (size_t)bt * N;
+    const uint32_t* cand = w.cand + (size_t)bt * kCap * 2;
+
+    // Threshold bin again (same histogram, same answer as the filter).
+    const uint32_t* gh = w.hist + (size_t)bt * kBins;
+    for (int i = threadIdx.x; i < kBins; i += kSelThreads)
+        hist[i] = gh[i];
+    __syncthreads();
+    uint32_t b1, above1;
+    find_bin_desc(hist, kBins, (uint32_t)k, b1, above1, s_wave, s_pick);
+
+    // Tile counts of every tile of this token (written by the filter).
+    __shared__ uint32_t s_def[kMaxTiles];
+    for (int i = threadIdx.x; i < nt_eff; i += kSelThreads)
+        s_def[i] = w.tile_def[(size_t)bt * NT + i];
+    uint32_t part = 0;
+    for (int i = threadIdx.x; i < nt_eff; i += kSelThreads)
+        part += w.tile_def[(size_t)bt * NT + i];
+    uint32_t above;
+    block_excl_scan(part, above, s_wave);
+    // above: keys in bins higher than the threshold bin, over all tiles.
+    const uint32_t need = (uint32_t)k - above;   // kept keys inside the bin, >= 1
+    const uint32_t nc = w.cand_n[bt];
+
+    uint32_t prefix = b1 << 21, pmask = 0xffe00000u, r = need;
+    uint32_t tau, cut;
+    for (int i = threadIdx.x; i < nt_eff; i += kSelThreads)
+        s_tile[i] = 0u;
+    if (nc <= (uint32_t)kCap) {
+#pragma unroll
+        for (int q = 0; q < kCap / kSelThreads; ++q) {
+            const int i = q * kSelThreads + (int)threadIdx.x;
+            if (i < (int)nc) {
+                const uint2 e = ((const uint2*)cand)[i];
+                c_key[i] = e.x;
+                c_idx[i] = e.y;
+            }
         }
-        run_gt += total & 0xffffu;
-        run_eq += total >> 16;
-        if (run_gt + min(run_eq, need) >= (uint32_t)k)
-            break;
+        __syncthreads();
+        radix_kth_largest((int)nc, [&](int i, uint32_t& v) { v = c_key[i]; return true; }, 1,
+                          prefix, pmask, r, hist, s_wave, s_pick);
+        tau = prefix;
+        uint32_t ip = 0u, im = 0u;   // r-th smallest index among keys == tau
+        radix_kth_largest((int)nc,
+                          [&](int i, uint32_t& v) {
+                              v = ~c_idx[i];
+                              return c_key[i] == tau;
+                          },
+                          0, ip, im, r, hist, s_wave, s_pick);
+        cut = ~ip;
+        for (int i = threadIdx.x; i < (int)nc; i += kSelThreads) {
+            const uint32_t u = c_key[i], j = c_idx[i];
+            if (u > tau || (u == tau && j <= cut))
+                atomicAdd(&s_tile[j / kTile], 1u);
+        }
+    } else {
+        // Too many keys share the threshold bin: stream the token's keys.
+        __syncthreads();
+        radix_kth_largest(nvis, [&](int i, uint32_t& v) { v = kr[i]; return true; }, 1, prefix,
+                          pmask, r, hist, s_wave, s_pick);
+        tau = prefix;
+        uint32_t ip = 0u, im = 0u;
+        radix_kth_largest(nvis,
+                          [&](int i, uint32_t& v) {
+                              v = ~(uint32_t)i;
+                              return kr[i] == tau;
+                          },
+                          0, ip, im, r, hist, s_wave, s_pick);
+        cut = ~ip;
+        for (int i = threadIdx.x; i < nvis; i += kSelThreads) {
+            const uint32_t u = kr[i];
+            if ((u >> 21) == b1 && (u > tau || (u == tau && (uint32_t)i <= cut)))
+                atomicAdd(&s_tile[i / kTile], 1u);
+        }
     }
-    for (int i = k + tid; i < cap; i += kSelThreads)
-        row[i] = -1;
-    if (tid == 0)
+    __syncthreads();
+    // Output offset of each tile: exclusive prefix of its kept count
+    // (kMaxTiles / kSelThreads = 4 consecutive tiles per thread).
+    uint32_t* to = w.tile_off + (size_t)bt * NT;
+    constexpr int TPT = kMaxTiles / kSelThreads;
+    uint32_t tsum = 0;
+    for (int i = 0; i < TPT; ++i) {
+        const int t = threadIdx.x * TPT + i;
+        tsum += (t < nt_eff) ? s_def[t] + s_tile[t] : 0u;
+    }
+    uint32_t ttot;
+    uint32_t off = block_excl_scan(tsum, ttot, s_wave);
+    for (int i = 0; i < TPT; ++i) {
+        const int t = threadIdx.x * TPT + i;
+        if (t < nt_eff) {
+            to[t] = off;
+            off += s_def[t] + s_tile[t];
+        }
+    }
+    if (threadIdx.x == 0) {
+        w.pivot[2 * bt] = tau;
+        w.pivot[2 * bt + 1] = cut;
         n_sel[bt] = k;
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_sel_write(SelWs w, int32_t* __restrict__ ids,
+                                                           int32_t* __restrict__ n_sel, int T,
+                                                           int N, int NT, int pos0, int k,
+                                                           int dense_max, int cap)
+{
+    const int bt = blockIdx.y;
+    const int nvis = pos0 + (bt % T) + 1;
+    const int tile = blockIdx.x;
+    const int j0 = tile * kTile;
+    int32_t* row = ids + (size_t)bt * cap;
+
+    if (!token_selects(nvis, k, dense_max)) {
+        // Keep every visible cell: ids 0..nvis-1, then -1.
+        if (tile == 0 && threadIdx.x == 0)
+            n_sel[bt] = nvis;
+        const int e0 = j0, e1 = min(j0 + kTile, cap);
+        for (int i = e0 + threadIdx.x; i < e1; i += kSelThreads)
+            row[i] = (i < nvis) ? i : -1;
+        return;
+    }
+    if (tile == 0)
+        for (int i = k + threadIdx.x; i < cap; i += kSelThreads)
+            row[i] = -1;
+    if (j0 >= nvis)
+        return;
+    const uint32_t tau = w.pivot[2 * bt], cut = w.pivot[2 * bt + 1];
+    const uint32_t base = w.tile_off[(size_t)bt * NT + tile];
+    const uint32_t* kr = w.keys + (size_t)bt * N;
+    // Each wave owns a contiguous quarter of the tile (so output order is
+    // wave order, then lane order): count its kept cells with ballots, then
+    // write them at their offsets.
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int j1 = min(j0 + kTile, nvis);
+    const int wb = j0 + wv * (kTile / 4);
+    uint32_t u[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int j = wb + i * 64 + lane;
+        u[i] = (j < j1) ? kr[j] : 0u;
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const uint32_t j = (uint32_t)(wb + i * 64 + lane);
+        const bool keep = (int)j < j1 && (u[i] > tau || (u[i] == tau && j <= cut));
+        cnt += (uint32_t)__popcll(__ballot(keep));
+    }
+    __shared__ uint32_t s_cnt[kSelThreads / 64];
+    if (lane == 0)
+        s_cnt[wv] = cnt;
+    __syncthreads();
+    uint32_t wpos = base;
+    for (int i = 0; i < wv; ++i)
+        wpos += s_cnt[i];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const uint32_t j = (uint32_t)(wb + i * 64 + lane);
+        const bool keep = (int)j < j1 && (u[i] > tau || (u[i] == tau && j <= cut));
+        const unsigned long long m = __ballot(keep);
+        const uint32_t pos = wpos + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (keep && pos < (uint32_t)k)
+            row[pos] = (int32_t)j;
+        wpos += (uint32_t)__popcll(m);
+    }
 }
 
 // ------------------------------------------------------------- launch ---
 
-size_t index_workspace_bytes(int B, int T, int N)
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static SelWs carve(void* ws, int B, int T, int N, size_t* total)
 {
-    return (size_t)B * (size_t)T * (size_t)N * sizeof(uint32_t);
+    const size_t BT = (size_t)B * T;
+    const int NT = (N + kTile - 1) / kTile;
+    char* p = (char*)ws;
+    size_t off = 0;
+    SelWs w;
+    auto take = [&](size_t bytes) {
+        char* q = p ? p + off : nullptr;
+        off += align256(bytes);
+        return q;
+    };
+    w.keys = (uint32_t*)take(BT * N * 4);
+    w.hist = (uint32_t*)take(BT * kBins * 4);
+    w.tile_def = (uint32_t*)take(BT * NT * 4);
+    w.tile_off = (uint32_t*)take(BT * NT * 4);
+    w.cand_n = (uint32_t*)take(BT * 4);
+    w.done = (uint32_t*)take(BT * 4);
+    w.cand = (uint32_t*)take(BT * kCap * 8);
+    w.pivot = (uint32_t*)take(BT * 8);
+    if (total)
+        *total = off;
+    return w;
 }
 
+size_t index_workspace_bytes(int B, int T, int N)
+{
+    size_t total = 0;
+    carve(nullptr, B, T, N, &total);
+    return total;
+}
+
+int index_max_cells() { return kMaxTiles * kTile; }
+
 template <int DI>
-static void launch_scan(const IndexLaunch& a, int nvis_max, hipStream_t s)
+static void launch_scan(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipStream_t s)
 {
     constexpr int rows_per_block = (256 / (DI / 8)) * 8;
     dim3 grid((nvis_max + rows_per_block - 1) / rows_per_block, a.B);
     const uint4* q = (const uint4*)a.q_idx;
     const uint4* K = (const uint4*)a.K_idx;
     if (a.T <= 1)
-        k_idx_scan<DI, 1><<<grid, 256, 0, s>>>(q, K, a.keys, a.T, a.N, nvis_max);
+        k_idx_scan<DI, 1><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
     else if (a.T <= 2)
-        k_idx_scan<DI, 2><<<grid, 256, 0, s>>>(q, K, a.keys, a.T, a.N, nvis_max);
+        k_idx_scan<DI, 2><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
     else if (a.T <= 4)
-        k_idx_scan<DI, 4><<<grid, 256, 0, s>>>(q, K, a.keys, a.T, a.N, nvis_max);
+        k_idx_scan<DI, 4><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
     else if (a.T <= 8)
-        k_idx_scan<DI, 8><<<grid, 256, 0, s>>>(q, K, a.keys, a.T, a.N, nvis_max);
+        k_idx_scan<DI, 8><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
     else
-        k_idx_scan<DI, 16><<<grid, 256, 0, s>>>(q, K, a.keys, a.T, a.N, nvis_max);
+        k_idx_scan<DI, 16><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
 }
 
 template <int DI>
-static void launch_gemm(const IndexLaunch& a, int nvis_max, hipStream_t s)
+static void launch_gemm(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipStream_t s)
 {
     dim3 grid((nvis_max + 63) / 64, (a.T + 63) / 64, a.B);
     k_idx_gemm<DI><<<grid, 256, 0, s>>>((const _Float16*)a.q_idx, (const _Float16*)a.K_idx,
-                                         a.keys, a.T, a.N, nvis_max);
+                                         keys, a.T, a.N, nvis_max);
 }
 
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
 {
+    SelWs w = carve(a.ws, a.B, a.T, a.N, nullptr);
+    const int BT = a.B * a.T;
+    const int NT = (a.N + kTile - 1) / kTile;
     // Scores are needed only when some token keeps fewer cells than it sees.
     const int nvis_max = a.pos0 + a.T;  // cells visible to the last token
-    const bool any_select = nvis_max > a.dense_max && nvis_max > a.k;
+    const bool any_select = token_selects(nvis_max, a.k, a.dense_max);
     if (any_select) {
         if (a.T <= 16) {
             if (a.DI == 64)
-                launch_scan<64>(a, nvis_max, s);
+                launch_scan<64>(a, w.keys, nvis_max, s);
             else
-                launch_scan<128>(a, nvis_max, s);
+                launch_scan<128>(a, w.keys, nvis_max, s);
         } else {
             if (a.DI == 64)
-                launch_gemm<64>(a, nvis_max, s);
+                launch_gemm<64>(a, w.keys, nvis_max, s);
             else
-                launch_gemm<128>(a, nvis_max, s);
+                launch_gemm<128>(a, w.keys, nvis_max, s);
         }
+        const int clear_blocks = (int)std::min<size_t>(((size_t)BT * kBins + 1023) / 1024, 4096);
+        k_sel_clear<<<clear_blocks, kSelThreads, 0, s>>>(w, BT);
+        const dim3 grid(NT, BT);
+        k_sel_hist<<<grid, kSelThreads, 0, s>>>(w, a.T, a.N, a.pos0, a.k, a.dense_max);
+        k_sel_filter<<<grid, kSelThreads, 0, s>>>(w, a.T, a.N, NT, a.pos0, a.k, a.dense_max);
+        k_sel_pivot<<<BT, kSelThreads, 0, s>>>(w, a.n_sel, a.T, a.N, NT, a.pos0, a.k,
+                                                 a.dense_max);
     }
-    k_select_row<<<dim3((unsigned)(a.B * a.T)), kSelThreads, 0, s>>>(
-        a.keys, a.ids, a.n_sel, a.T, a.N, a.pos0, a.k, a.dense_max, a.cap);
+    const int NTw = std::max(NT, (a.cap + kTile - 1) / kTile);
+    k_sel_write<<<dim3(NTw, BT), kSelThreads, 0, s>>>(w, a.ids, a.n_sel, a.T, a.N, NT, a.pos0,
+                                                       a.k, a.dense_max, a.cap);
     return hipGetLastError();
 }
 

@@ -15,11 +15,14 @@ struct IndexLaunch {
     const void* K_idx;
     int32_t* ids;
     int32_t* n_sel;
-    uint32_t* keys;  // workspace: [B][T][N] score keys
+    void* ws;  // workspace of index_workspace_bytes(B, T, N) bytes
 };
 
-// Bytes of workspace the index path needs.
+// Bytes of workspace the index path needs (score keys, histograms,
+// candidates, per-tile counts).
 size_t index_workspace_bytes(int B, int T, int N);
+// Largest n_cells the select kernels handle.
+int index_max_cells();
 
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s);
 
