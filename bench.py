@@ -65,6 +65,31 @@ def attend_flops(p: dict, n_sel_total: int) -> float:
     return float(n_sel_total) * p["Hq"] * p["D"] * 4      # QK + PV FMAs, 2 flop each
 
 
+def profiled_traffic(workload: str, B: int, P: int):
+    """HBM bytes per k_attend dispatch from the committed rocprofv3 summary of
+    this exact launch configuration (profiles/<workload>_b<B>_P<P>.md), scaled
+    by the copy-kernel calibration recorded there; None if there is no such
+    summary or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_b{B}_P{P}.md")
+    src = os.path.join(ROOT, "top_sparse_attention_score_amd", "csrc", "qsa_attend.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`")):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("traffic_source_sha256_16") != sha:
+        return None
+    try:
+        return int(fields["k_attend_read_bytes_per_dispatch"]) + \
+            int(fields["k_attend_write_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp_cfg: str, target_s: float, P: int) -> dict:
     """The oracle (plain C, double, one thread) on as many problems of the same
     workload as fit in about target_s seconds."""
@@ -181,7 +206,9 @@ def main() -> None:
         achieved = flops / (stage_ms[1] * 1e-3) / 1e12
         roof = dict(kernel="k_attend", bound="alu", achieved=round(achieved, 2),
                     peak=round(FP32_VALU_PEAK_TFLOPS, 1), unit="TFLOP/s",
-                    frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4), traffic=None,
+                    frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4),
+                    traffic=profiled_traffic(args.workload, B, P),
+                    algorithmic_bytes=by["attend"],
                     hbm_gbs=round(by["attend"] / (stage_ms[1] * 1e-3) / 1e9, 1))
     else:
         sb = by["index"] if names[dom] == "index_topk" else by["out"]
