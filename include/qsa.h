@@ -62,6 +62,13 @@ typedef enum {
 
 typedef enum { QSA_F32 = 0, QSA_F16 = 1 } qsa_dtype;
 
+/* Kernel family of qsa_attend (qsa_attn_desc.algo). */
+typedef enum {
+    QSA_ATTEND_AUTO = 0,    /* currently QSA_ATTEND_MATRIX */
+    QSA_ATTEND_MATRIX = 1,  /* matrix cores (MFMA) with split fp16 operands */
+    QSA_ATTEND_VECTOR = 2   /* fp32 vector FMAs */
+} qsa_attend_algo;
+
 /* Static description of a status code (never NULL). */
 QSA_API const char* qsa_status_string(int status);
 
@@ -125,7 +132,17 @@ QSA_API int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const 
  * and head h, with x_j = scale * sum_d q[h][d] * Kq[j][g][d] * Ksc[j][g][d/32]:
  *   m = max_j x_j,   l = sum_j exp(x_j - m),
  *   o[d] = sum_j exp(x_j - m) * Vq[j][g][d] * Vsc[j][g][d/32]   (unnormalised)
- * An empty chunk gives m = -inf, l = 0, o = 0.  Arithmetic is fp32.
+ * An empty chunk gives m = -inf, l = 0, o = 0.
+ *
+ * Arithmetic.  QSA_ATTEND_VECTOR evaluates the definition with fp32 FMAs.
+ * QSA_ATTEND_MATRIX (the default) runs both products on the matrix cores
+ * with fp16 operands that carry the fp32 values: int8 codes are exact in
+ * fp16; an fp32 query element and each weight exp(x_j - m) * Vsc are split
+ * into two fp16 halves (hi + lo, 22 significant bits) whose products
+ * accumulate in fp32.  Its results agree with the fp32 definition to
+ * within about 1e-6 relative to the output scale.  It requires finite
+ * |q| < 65504 and |Vsc| < 255 (larger values overflow the fp16 halves and
+ * give non-finite output); fp16 queries are used as given.
  *
  * Inputs
  *   q      [B][T][Hq][D], fp32 (q_dtype QSA_F32) or fp16 (QSA_F16), 16-byte
@@ -165,6 +182,7 @@ typedef struct qsa_attn_desc {
     float scale;         /* softmax scale, e.g. 1/sqrt(D) */
     int q_dtype;         /* qsa_dtype of q */
     int out_dtype;       /* qsa_dtype of the merged output */
+    int algo;            /* qsa_attend_algo; 0 (zero-initialised) = default */
     long long kq_cell_stride, ksc_cell_stride, vq_cell_stride, vsc_cell_stride;
     long long kq_batch_stride, ksc_batch_stride, vq_batch_stride, vsc_batch_stride;
 } qsa_attn_desc;

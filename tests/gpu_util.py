@@ -26,10 +26,14 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
+# qsa_attend kernel families exercised by the parity tests
+ALGOS = {"matrix": qsa.QSA_ATTEND_MATRIX, "vector": qsa.QSA_ATTEND_VECTOR}
+
+
 def run_gpu(inp: dict, *, P: int | None = None, strides=None, dev=None, ids=None,
-            n_sel=None, index=True) -> dict:
+            n_sel=None, index=True, algo: str = "matrix") -> dict:
     """Runs index_topk -> attend -> merge on cuda:0 and returns numpy copies."""
-    path = qsa.path_for(inp, P=P, strides=strides)
+    path = qsa.path_for(inp, P=P, strides=strides, algo=ALGOS[algo])
     dev = qsa.to_device(inp) if dev is None else dev
     if index:
         path.index(dev["q_idx"], dev["K_idx"])

@@ -120,6 +120,7 @@ def test_index_pointer_and_workspace_checks():
     (dict(strides=dict(ksc_cell_stride=34)), INVALID),
     (dict(strides=dict(vq_batch_stride=8)), INVALID),
     (dict(strides=dict(kq_cell_stride=-16)), INVALID),
+    (dict(algo=3), INVALID), (dict(algo=-1), INVALID),
 ])
 def test_attn_desc_rejected(kw, code):
     d = _adesc(**kw)

@@ -28,24 +28,26 @@ def _oracle_all(orc, inp, P):
 
 # ------------------------------------------------------------ workloads ---
 
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
 @pytest.mark.parametrize("cfg,batch", [("tiny", 3), ("decode", 2), ("draft", 1), ("long", 1)])
-def test_workload_parity(orc, cfg, batch):
+def test_workload_parity(orc, cfg, batch, algo):
     inp = make_inputs(cfg, seed=1000 + batch, batch=batch)
-    say(f"[parity] {cfg} B={batch} T={inp['T']} N={inp['N']} P={inp['P']}")
-    res = run_gpu(inp)
+    say(f"[parity] {cfg} B={batch} T={inp['T']} N={inp['N']} P={inp['P']} {algo}")
+    res = run_gpu(inp, algo=algo)
     ref = _oracle_all(orc, inp, inp["P"])
     assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
     assert_partials_close(res, ref["pm"], ref["pl"], ref["po"])
     assert_out_close(res["out"], ref["out"])
 
 
-def test_prompt_chunk_sampled(orc):
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+def test_prompt_chunk_sampled(orc, algo):
     """The 2048-token prompt chunk at full size on the GPU; the oracle checks
     sampled tokens one by one, and every token's kept set is checked against
     exact float64 scores (a property that holds at any size)."""
     inp = make_inputs("prompt", seed=1005)
-    say("[parity] prompt T=2048 N=65536 full size")
-    res = run_gpu(inp)
+    say(f"[parity] prompt T=2048 N=65536 full size {algo}")
+    res = run_gpu(inp, algo=algo)
     T, pos0, k = inp["T"], inp["pos0"], inp["k"]
     assert np.all(res["n_sel"] == k)
     S = inp["q_idx"][0].astype(np.float64) @ inp["K_idx"][0].astype(np.float64).T
@@ -83,33 +85,37 @@ def test_pos_sweep(orc):
         assert_out_close(res["out"], ref["out"], f"pos0={pos0} ntok={ntok}")
 
 
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16, 64])
-def test_split_counts(orc, P):
+def test_split_counts(orc, P, algo):
     inp = make_inputs("decode", seed=3000 + P, batch=1)
-    say(f"[split] P={P}")
-    res = run_gpu(inp, P=P)
+    say(f"[split] P={P} {algo}")
+    res = run_gpu(inp, P=P, algo=algo)
     ref = _oracle_all(orc, inp, P)
     assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
     assert_partials_close(res, ref["pm"], ref["pl"], ref["po"])
     assert_out_close(res["out"], ref["out"])
 
 
-@pytest.mark.parametrize("n_max", [1, 5, 64, 65, 300, 2051])
-def test_attend_scattered_ids(orc, n_max):
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+@pytest.mark.parametrize("n_max", [1, 5, 31, 32, 33, 64, 65, 300, 2051])
+def test_attend_scattered_ids(orc, n_max, algo):
     """Attention and merge alone on random scattered ids (decoupled from the
-    indexer), per the pages' bitwise-check input."""
+    indexer), per the pages' bitwise-check input; chunk lengths straddle the
+    32-cell tile of the matrix kernel."""
     inp = make_inputs("decode", seed=4000 + n_max, batch=2, N=32768, T=4, pos0=30000)
     ids, n_sel = scattered_ids(seed=5, batch=2, T=4, N=32768, cap=inp["cap"], pos0=30000,
                                n_max=n_max)
-    say(f"[scattered] n_max={n_max}")
-    res = run_gpu(inp, ids=ids, n_sel=n_sel, index=False)
+    say(f"[scattered] n_max={n_max} {algo}")
+    res = run_gpu(inp, ids=ids, n_sel=n_sel, index=False, algo=algo)
     pm, pl, po = orc.attend(inp["q"], inp["Kq"], inp["Ksc"], inp["Vq"], inp["Vsc"], ids,
                             n_sel, P=inp["P"], scale=1 / 16)
     assert_partials_close(res, pm, pl, po)
     assert_out_close(res["out"], orc.merge(pm, pl, po))
 
 
-def test_tiny_fp16_and_gqa_variants(orc):
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+def test_tiny_fp16_and_gqa_variants(orc, algo):
     """Every supported (G, D) pair with fp32 and fp16 queries on small inputs."""
     for D in (64, 256):
         for G in (1, 2, 4, 8, 12, 16):
@@ -118,8 +124,8 @@ def test_tiny_fp16_and_gqa_variants(orc):
                 cfg = dict(T=2, N=700, di=64, k=150, dense_max=153, Hq=G * Hkv, Hkv=Hkv,
                            D=D, P=3, q_dtype=qd, out_dtype=qd, heavy_tail=False)
                 inp = make_inputs(cfg, seed=G * 10 + D)
-                say(f"[variant] D={D} G={G} q={qd}")
-                res = run_gpu(inp)
+                say(f"[variant] D={D} G={G} q={qd} {algo}")
+                res = run_gpu(inp, algo=algo)
                 ref = _oracle_all(orc, inp, 3)
                 assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
                 assert_out_close(res["out"], ref["out"], f"D={D} G={G} {qd}")
@@ -183,37 +189,41 @@ def test_interleaved_cache_layout(orc):
 
 # ------------------------------------------------ the pages' bit claims ---
 
-def test_padding_beyond_n_sel_is_ignored():
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+def test_padding_beyond_n_sel_is_ignored(algo):
     """Entries past n_sel never change the partials (an absent cell adds
     p = 0): garbage padding gives bitwise-identical partials and output."""
     inp = make_inputs("decode", seed=81, batch=2, N=16384, T=3, pos0=16000)
     ids, n_sel = scattered_ids(seed=9, batch=2, T=3, N=16384, cap=inp["cap"], pos0=16000,
                                n_max=1000)
-    a = run_gpu(inp, ids=ids, n_sel=n_sel, index=False)
+    a = run_gpu(inp, ids=ids, n_sel=n_sel, index=False, algo=algo)
     ids2 = ids.copy()
     rng = np.random.default_rng(10)
     for b in range(2):
         for t in range(3):
             n = n_sel[b, t]
             ids2[b, t, n:] = rng.integers(0, 16384, size=ids2.shape[-1] - n)
-    b_ = run_gpu(inp, ids=ids2, n_sel=n_sel, index=False)
+    b_ = run_gpu(inp, ids=ids2, n_sel=n_sel, index=False, algo=algo)
     for key in ("pm", "pl", "po", "out"):
         assert a[key].tobytes() == b_[key].tobytes(), key
 
 
-def test_run_to_run_determinism():
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+def test_run_to_run_determinism(algo):
     inp = make_inputs("draft", seed=82, N=16384)
-    a = run_gpu(inp)
-    b = run_gpu(inp)
+    a = run_gpu(inp, algo=algo)
+    b = run_gpu(inp, algo=algo)
     for key in ("ids", "n_sel", "pm", "pl", "po", "out"):
         assert a[key].tobytes() == b[key].tobytes(), key
 
 
-def test_position_zero_is_exact():
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+def test_position_zero_is_exact(algo):
     """A token at position 0 keeps only cell 0 and its output is that cell's
-    dequantised V row, bit for bit (exp(0) = 1, fma(1, v, 0) = v, v / 1 = v)."""
+    dequantised V row, bit for bit (exp(0) = 1, the weight 1 times an fp16
+    scale and an int8 code is exact in either kernel, v / 1 = v)."""
     inp = make_inputs("decode", seed=83, batch=2, N=64, T=1, pos0=0)
-    res = run_gpu(inp)
+    res = run_gpu(inp, algo=algo)
     assert np.all(res["n_sel"] == 1) and np.all(res["ids"][:, :, 0] == 0)
     v = (inp["Vq"][:, 0].astype(np.float64) *
          np.repeat(inp["Vsc"][:, 0].astype(np.float64), 32, axis=-1)).astype(np.float32)
@@ -222,12 +232,13 @@ def test_position_zero_is_exact():
         assert res["out"][:, 0, h].tobytes() == v[:, h // G].tobytes()
 
 
-def test_chunk_max_is_exact_max_of_logits():
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+def test_chunk_max_is_exact_max_of_logits(algo):
     """The partial max of a one-cell chunk is that cell's logit, and the max
     of a chunk equals the max over its one-cell chunks bit for bit."""
     inp = make_inputs("decode", seed=84, batch=1, N=4096, T=1, pos0=4095, k=64,
                       dense_max=67)
-    one = run_gpu(inp, P=64)          # 64 ids -> 64 one-cell chunks
-    whole = run_gpu(inp, P=1)
+    one = run_gpu(inp, P=64, algo=algo)          # 64 ids -> 64 one-cell chunks
+    whole = run_gpu(inp, P=1, algo=algo)
     assert np.all(one["pl"] == 1.0)
     assert whole["pm"][..., 0].tobytes() == one["pm"].max(axis=-1).tobytes()

@@ -45,6 +45,8 @@ int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
     if ((d->q_dtype != QSA_F32 && d->q_dtype != QSA_F16) ||
         (d->out_dtype != QSA_F32 && d->out_dtype != QSA_F16))
         return QSA_ERR_INVALID_ARG;
+    if (d->algo < QSA_ATTEND_AUTO || d->algo > QSA_ATTEND_VECTOR)
+        return QSA_ERR_INVALID_ARG;
     if (d->P > 64)
         return QSA_ERR_UNSUPPORTED;
     if (!qsa::attend_supported(d->Hq / d->Hkv, d->D))
@@ -83,6 +85,7 @@ int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
     L->scale = d->scale;
     L->q_f16 = d->q_dtype == QSA_F16;
     L->out_f16 = d->out_dtype == QSA_F16;
+    L->algo = d->algo;
     return QSA_OK;
 }
 

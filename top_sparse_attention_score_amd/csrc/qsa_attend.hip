@@ -32,8 +32,6 @@
 
 namespace qsa {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // Loads N consecutive wave-uniform 32-bit words starting at element `off`.
 // The offset passes through an empty asm so the loads stay where they are
 // written (they are not merged with, or hoisted next to, other heads' loads).
@@ -44,17 +42,6 @@ __device__ __forceinline__ void load_uniform(const T* __restrict__ base, size_t 
 #pragma unroll
     for (int e = 0; e < N; ++e)
         dst[e] = base[off + e];
-}
-
-// Signed bytes 2*half_sel and 2*half_sel+1 of w as an exact fp16 pair:
-// (b + 128) is placed in the low mantissa byte of 1024.0 (0x6400), giving
-// 1024 + 128 + b exactly, and 1152 is subtracted in packed fp16.
-__device__ __forceinline__ half2_t int8_pair_to_half2(int w, int half_sel)
-{
-    const uint32_t u = (uint32_t)w ^ 0x80808080u;
-    const uint32_t sel = half_sel ? 0x04030402u : 0x04010400u;
-    const uint32_t bits = __builtin_amdgcn_perm(0x64646464u, u, sel);
-    return as_half2(bits) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
 }
 
 // Copies the V codes (D bytes) and V scales (D/16 bytes) of the tile's 64
@@ -85,15 +72,6 @@ __device__ __forceinline__ void dma_v_tile(const char* Vb, long long vq_cs, cons
 }
 
 constexpr int kAttendWaves = 4;  // chunks of one (token, KV head) per workgroup
-
-// Orders this wave's LDS accesses: every earlier LDS access has completed and
-// all lanes of the wave have reached this point.  The waves of a workgroup
-// never share LDS, so no workgroup barrier is needed.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
-}
 
 template <int G, int D, bool QF16>
 __global__ __launch_bounds__(64 * kAttendWaves) void k_attend(
@@ -436,7 +414,11 @@ bool attend_supported(int G, int D)
 hipError_t launch_attend(const AttnLaunch& a, hipStream_t s)
 {
     const int G = a.Hq / a.Hkv;
-    const bool ok = (a.D == 64) ? launch_attend_d<64>(a, G, s) : launch_attend_d<256>(a, G, s);
+    bool ok;
+    if (a.algo == 2)  // vector fp32 kernel
+        ok = (a.D == 64) ? launch_attend_d<64>(a, G, s) : launch_attend_d<256>(a, G, s);
+    else
+        ok = launch_attend_mma(a, s);
     if (!ok)
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -30,6 +30,7 @@ struct AttnLaunch {
     int B, T, Hq, Hkv, D, P, cap, N;
     float scale;
     bool q_f16, out_f16;
+    int algo;  // qsa_attend_algo
     const void* q;
     const int8_t* Kq;
     const void* Ksc;
@@ -49,6 +50,8 @@ struct AttnLaunch {
 bool attend_supported(int G, int D);
 
 hipError_t launch_attend(const AttnLaunch& a, hipStream_t s);
+// Matrix-core attend kernel (qsa_attend_mma.hip); false if no variant fits.
+bool launch_attend_mma(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_merge(const AttnLaunch& a, hipStream_t s);
 
 }  // namespace qsa

@@ -19,6 +19,10 @@ LIB_PATH = os.path.join(_HERE, "libqsa.so")
 
 QSA_F32 = 0
 QSA_F16 = 1
+# qsa_attend kernel families (qsa_attend_algo)
+QSA_ATTEND_AUTO = 0
+QSA_ATTEND_MATRIX = 1
+QSA_ATTEND_VECTOR = 2
 
 _c_int, _c_ll, _c_float, _vp = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p
 
@@ -36,7 +40,7 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", _c_int), ("T", _c_int), ("Hq", _c_int), ("Hkv", _c_int),
                 ("D", _c_int), ("P", _c_int), ("ids_cap", _c_int), ("n_cells", _c_int),
                 ("scale", _c_float), ("q_dtype", _c_int), ("out_dtype", _c_int),
-                ("kq_cell_stride", _c_ll), ("ksc_cell_stride", _c_ll),
+                ("algo", _c_int), ("kq_cell_stride", _c_ll), ("ksc_cell_stride", _c_ll),
                 ("vq_cell_stride", _c_ll), ("vsc_cell_stride", _c_ll),
                 ("kq_batch_stride", _c_ll), ("ksc_batch_stride", _c_ll),
                 ("vq_batch_stride", _c_ll), ("vsc_batch_stride", _c_ll)]
@@ -102,11 +106,12 @@ def index_desc(*, batch: int, T: int, n_cells: int, d_idx: int, k: int, pos0: in
 
 def attn_desc(*, batch: int, T: int, Hq: int, Hkv: int, D: int, P: int, ids_cap: int,
               n_cells: int, scale: float | None = None, q_dtype: int = QSA_F32,
-              out_dtype: int = QSA_F32, strides: dict | None = None) -> AttnDesc:
+              out_dtype: int = QSA_F32, strides: dict | None = None,
+              algo: int = 0) -> AttnDesc:
     """Attention descriptor; `strides` may set any of the *_cell_stride /
     *_batch_stride fields (bytes); unset ones keep the dense default."""
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    d = AttnDesc(batch, T, Hq, Hkv, D, P, ids_cap, n_cells, sc, q_dtype, out_dtype)
+    d = AttnDesc(batch, T, Hq, Hkv, D, P, ids_cap, n_cells, sc, q_dtype, out_dtype, algo)
     for key, val in (strides or {}).items():
         setattr(d, key, int(val))
     return d
@@ -150,13 +155,15 @@ class QsaPath:
     """
 
     def __init__(self, *, batch, T, N, di, k, pos0, dense_max, cap, Hq, Hkv, D, P,
-                 q_f16=False, out_f16=False, scale=None, device="cuda", strides=None):
+                 q_f16=False, out_f16=False, scale=None, device="cuda", strides=None,
+                 algo=QSA_ATTEND_AUTO):
         self.idesc = index_desc(batch=batch, T=T, n_cells=N, d_idx=di, k=k, pos0=pos0,
                                 dense_max=dense_max, ids_cap=cap)
         self.adesc = attn_desc(batch=batch, T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, ids_cap=cap,
                                n_cells=N, scale=scale,
                                q_dtype=QSA_F16 if q_f16 else QSA_F32,
-                               out_dtype=QSA_F16 if out_f16 else QSA_F32, strides=strides)
+                               out_dtype=QSA_F16 if out_f16 else QSA_F32, strides=strides,
+                               algo=algo)
         ws_bytes = qsa_index_topk_workspace(self.idesc)
         n_part = qsa_partials_floats(self.adesc)
         if ws_bytes == 0 or n_part == 0:
@@ -198,10 +205,12 @@ def to_device(inp: dict, device="cuda") -> dict:
     return out
 
 
-def path_for(inp: dict, *, P: int | None = None, device="cuda", strides=None) -> QsaPath:
+def path_for(inp: dict, *, P: int | None = None, device="cuda", strides=None,
+             algo: int = QSA_ATTEND_AUTO) -> QsaPath:
     """A QsaPath sized for an input dict produced by the seeded generator."""
     return QsaPath(batch=inp["batch"], T=inp["T"], N=inp["N"], di=inp["di"], k=inp["k"],
                    pos0=inp["pos0"], dense_max=inp["dense_max"], cap=inp["cap"],
                    Hq=inp["Hq"], Hkv=inp["Hkv"], D=inp["D"],
                    P=inp["P"] if P is None else P, q_f16=inp["q_dtype"] == "f16",
-                   out_f16=inp["out_dtype"] == "f16", device=device, strides=strides)
+                   out_f16=inp["out_dtype"] == "f16", device=device, strides=strides,
+                   algo=algo)
