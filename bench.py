@@ -65,14 +65,20 @@ def attend_flops(p: dict, n_sel_total: int) -> float:
     return float(n_sel_total) * p["Hq"] * p["D"] * 4      # QK + PV FMAs, 2 flop each
 
 
-def profiled_traffic(workload: str, B: int, P: int):
-    """HBM bytes per k_attend dispatch from the committed rocprofv3 summary of
-    this exact launch configuration (profiles/<workload>_b<B>_P<P>.md), scaled
-    by the copy-kernel calibration recorded there; None if there is no such
-    summary or the kernel source changed since it was taken."""
+# Source file of each attend kernel family (its hash gates profiled traffic).
+ATTEND_SOURCES = {"matrix": "qsa_attend_mma.hip", "vector": "qsa_attend.hip"}
+ATTEND_KERNELS = {"matrix": "k_attend_mma", "vector": "k_attend"}
+
+
+def profiled_traffic(workload: str, B: int, P: int, algo: str):
+    """HBM bytes per attend dispatch from the committed rocprofv3 summary of
+    this exact launch configuration (profiles/<kernel>_<workload>_b<B>_P<P>.md),
+    scaled by the copy-kernel calibration recorded there; None if there is no
+    such summary or the kernel source changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{workload}_b{B}_P{P}.md")
-    src = os.path.join(ROOT, "top_sparse_attention_score_amd", "csrc", "qsa_attend.hip")
+    kern = ATTEND_KERNELS[algo]
+    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_b{B}_P{P}.md")
+    src = os.path.join(ROOT, "top_sparse_attention_score_amd", "csrc", ATTEND_SOURCES[algo])
     if not os.path.exists(path):
         return None
     fields = {}
@@ -84,8 +90,7 @@ def profiled_traffic(workload: str, B: int, P: int):
     if fields.get("traffic_source_sha256_16") != sha:
         return None
     try:
-        return int(fields["k_attend_read_bytes_per_dispatch"]) + \
-            int(fields["k_attend_write_bytes_per_dispatch"])
+        return int(fields["read_bytes_per_dispatch"]) + int(fields["write_bytes_per_dispatch"])
     except (KeyError, ValueError):
         return None
 
@@ -128,6 +133,8 @@ def main() -> None:
                     help="distinct seeded problems, tiled to the batch on the GPU")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--algo", default="matrix", choices=["matrix", "vector"],
+                    help="qsa_attend kernel family")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB "
                          "(a known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -157,7 +164,8 @@ def main() -> None:
         dev[key] = t.repeat((reps,) + (1,) * (t.dim() - 1))[:B].contiguous()
     inp = dict(base)
     inp["batch"] = B
-    path = qsa.path_for(inp, P=P)
+    algo_code = qsa.QSA_ATTEND_MATRIX if args.algo == "matrix" else qsa.QSA_ATTEND_VECTOR
+    path = qsa.path_for(inp, P=P, algo=algo_code)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 18        # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -202,14 +210,23 @@ def main() -> None:
     # Dominant kernel: the stage with the largest average time.
     names = ["index_topk", "attend", "merge"]
     dom = int(np.argmax(stage_ms))
-    if names[dom] == "attend":
+    if names[dom] == "attend" and args.algo == "vector":
         achieved = flops / (stage_ms[1] * 1e-3) / 1e12
         roof = dict(kernel="k_attend", bound="alu", achieved=round(achieved, 2),
                     peak=round(FP32_VALU_PEAK_TFLOPS, 1), unit="TFLOP/s",
                     frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4),
-                    traffic=profiled_traffic(args.workload, B, P),
+                    traffic=profiled_traffic(args.workload, B, P, args.algo),
                     algorithmic_bytes=by["attend"],
                     hbm_gbs=round(by["attend"] / (stage_ms[1] * 1e-3) / 1e9, 1))
+    elif names[dom] == "attend":
+        # Matrix kernel: the products run on the matrix cores far below
+        # their peak; the gathers of the kept cells bound it.
+        achieved = by["attend"] / (stage_ms[1] * 1e-3) / 1e9
+        roof = dict(kernel="k_attend_mma", bound="hbm", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=profiled_traffic(args.workload, B, P, args.algo),
+                    algorithmic_bytes=by["attend"],
+                    definition_tflops=round(flops / (stage_ms[1] * 1e-3) / 1e12, 2))
     else:
         sb = by["index"] if names[dom] == "index_topk" else by["out"]
         achieved = sb / (stage_ms[dom] * 1e-3) / 1e9
@@ -223,7 +240,7 @@ def main() -> None:
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": desc, "batch": B, "T": inp["T"], "n_cells": inp["N"],
                    "k": inp["k"], "P": P, "d_idx": inp["di"], "heads": f"{inp['Hq']}x{inp['D']}",
-                   "kv_heads": inp["Hkv"]},
+                   "kv_heads": inp["Hkv"], "attend_kernel": args.algo},
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": by["total"],
         "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(names, stage_ms)},
