@@ -611,6 +611,165 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_write(SelWs w, int32_t* __r
     }
 }
 
+// ------------------------------------------------- single-block select ---
+//
+// Rows of at most kRowThreads * KPT cells are selected by one workgroup per
+// token: thread t holds the keys of cells t*KPT .. t*KPT+KPT-1 in registers,
+// a radix select over them (digits of 11, 11 and 10 bits, LDS histograms)
+// finds the k-th largest key v and how many keys equal to v are kept (the
+// lowest cells first), and two block-wide prefix sums give every thread the
+// output position of its kept cells, so the ids come out in ascending order.
+// Cells past the token's position hold key 0, below every score key.
+
+constexpr int kRowThreads = 1024;
+
+// Exclusive prefix sum over the kRowThreads threads; `total` gets the sum.
+__device__ __forceinline__ uint32_t row_excl_scan(uint32_t v, uint32_t& total,
+                                                  uint32_t* s_wave)
+{
+    constexpr int NW = kRowThreads / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        s_wave[w] = x;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t sv = s_wave[i];
+        base += (i < w) ? sv : 0u;
+        tot += sv;
+    }
+    __syncthreads();
+    total = tot;
+    return base + x - v;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kRowThreads) void k_sel_row(const uint32_t* __restrict__ keys,
+                                                         int32_t* __restrict__ ids,
+                                                         int32_t* __restrict__ n_sel, int T, int N,
+                                                         int pos0, int k, int dense_max, int cap)
+{
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t s_wave[kRowThreads / 64];
+    __shared__ uint32_t s_pick[2];
+    const int row = blockIdx.x;
+    const int nvis = pos0 + (row % T) + 1;
+    const int tid = threadIdx.x;
+    int32_t* out = ids + (size_t)row * cap;
+
+    if (!token_selects(nvis, k, dense_max)) {
+        // Keep every visible cell: ids 0..nvis-1, then -1.
+        if (tid == 0)
+            n_sel[row] = nvis;
+        for (int i = tid; i < cap; i += kRowThreads)
+            out[i] = (i < nvis) ? i : -1;
+        return;
+    }
+
+    const int c0 = tid * KPT;
+    const uint32_t* kr = keys + (size_t)row * N + c0;
+    uint32_t key[KPT];
+    if ((N & 3) == 0 && c0 + KPT <= nvis) {
+#pragma unroll
+        for (int j = 0; j < KPT; j += 4) {
+            const uint4 v = *(const uint4*)(kr + j);
+            key[j] = v.x;
+            key[j + 1] = v.y;
+            key[j + 2] = v.z;
+            key[j + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            key[j] = (c0 + j < nvis) ? kr[j] : 0u;
+    }
+
+    // Radix select of the k-th largest key.
+    uint32_t prefix = 0, pmask = 0, r = (uint32_t)k;
+#pragma unroll 1
+    for (int d = 0; d < 3; ++d) {
+        const int shift = (d == 0) ? 21 : (d == 1) ? 10 : 0;
+        const int nb = (d == 2) ? 1024 : 2048;
+        for (int i = tid; i < nb; i += kRowThreads)
+            hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if ((key[j] & pmask) == prefix)
+                atomicAdd(&hist[(key[j] >> shift) & (uint32_t)(nb - 1)], 1u);
+        __syncthreads();
+        // Bin holding the r-th largest: thread t sums bins nb-1-2t and
+        // nb-2-2t (nb / kRowThreads = 2 or 1 bins per thread).
+        const int per = nb / kRowThreads;
+        const int hi = nb - 1 - tid * per;
+        uint32_t sum = 0;
+        for (int i = 0; i < per; ++i)
+            sum += hist[hi - i];
+        uint32_t total;
+        const uint32_t ex = row_excl_scan(sum, total, s_wave);
+        if (ex < r && r <= ex + sum) {
+            uint32_t acc = ex;
+            for (int i = 0; i < per; ++i) {
+                const uint32_t cnt = hist[hi - i];
+                if (acc < r && r <= acc + cnt) {
+                    s_pick[0] = (uint32_t)(hi - i);
+                    s_pick[1] = acc;
+                }
+                acc += cnt;
+            }
+        }
+        __syncthreads();
+        r -= s_pick[1];
+        prefix |= s_pick[0] << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        __syncthreads();
+    }
+
+    // prefix is the k-th largest key; r keys equal to it are kept, lowest
+    // cells first.
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        gt += key[j] > prefix ? 1u : 0u;
+        eq += key[j] == prefix ? 1u : 0u;
+    }
+    uint32_t total;
+    const uint32_t eq_before = row_excl_scan(eq, total, s_wave);
+    const uint32_t take_eq = eq_before >= r ? 0u : min(eq, r - eq_before);
+    const uint32_t pos = row_excl_scan(gt + take_eq, total, s_wave);
+    uint32_t o = pos, taken = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const bool is_eq = key[j] == prefix;
+        const bool keep = key[j] > prefix || (is_eq && taken < take_eq);
+        taken += is_eq ? 1u : 0u;
+        if (keep)
+            out[o++] = c0 + j;
+    }
+    for (int i = k + tid; i < cap; i += kRowThreads)
+        out[i] = -1;
+    if (tid == 0)
+        n_sel[row] = k;
+}
+
+// Keys per thread of the single-block select for rows of N cells (0 if a row
+// is too long for it).
+static int row_select_kpt(int N)
+{
+    for (int kpt = 4; kpt <= 64; kpt *= 2)
+        if ((long long)kRowThreads * kpt >= N)
+            return kpt;
+    return 0;
+}
+
 // ------------------------------------------------------------- launch ---
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -695,6 +854,19 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
                 launch_gemm<64>(a, w.keys, nvis_max, s);
             else
                 launch_gemm<128>(a, w.keys, nvis_max, s);
+        }
+        const int kpt = row_select_kpt(a.N);
+        if (kpt) {
+#define QSA_ROW_ARGS w.keys, a.ids, a.n_sel, a.T, a.N, a.pos0, a.k, a.dense_max, a.cap
+            switch (kpt) {
+            case 4: k_sel_row<4><<<BT, kRowThreads, 0, s>>>(QSA_ROW_ARGS); break;
+            case 8: k_sel_row<8><<<BT, kRowThreads, 0, s>>>(QSA_ROW_ARGS); break;
+            case 16: k_sel_row<16><<<BT, kRowThreads, 0, s>>>(QSA_ROW_ARGS); break;
+            case 32: k_sel_row<32><<<BT, kRowThreads, 0, s>>>(QSA_ROW_ARGS); break;
+            default: k_sel_row<64><<<BT, kRowThreads, 0, s>>>(QSA_ROW_ARGS); break;
+            }
+#undef QSA_ROW_ARGS
+            return hipGetLastError();
         }
         const int clear_blocks = (int)std::min<size_t>(((size_t)BT * kBins + 1023) / 1024, 4096);
         k_sel_clear<<<clear_blocks, kSelThreads, 0, s>>>(w, BT);
