@@ -339,38 +339,58 @@ __global__ __launch_bounds__(64 * kAttendWaves) void k_attend(
     }
 }
 
-// One workgroup of D threads per (token, query head) row; thread d merges
-// output element d.
+constexpr int kMergeWaves = 4;
+
+// D/4 lanes per (token, query head) row, 4 consecutive output elements per
+// lane (float4 loads of every chunk's partial row); a wave covers 64/(D/4)
+// rows.  Per element: M = max_c m_c, then over the chunks in order
+// e = exp(m_c - M), L = fma(l_c, e, L), y = fma(o_c, e, y), and one division.
 template <int D, bool OUTF16>
-__global__ __launch_bounds__(D) void k_merge(const float* __restrict__ pm,
-                                             const float* __restrict__ pl,
-                                             const float* __restrict__ po,
-                                             void* __restrict__ out, int P)
+__global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restrict__ pm,
+                                                            const float* __restrict__ pl,
+                                                            const float* __restrict__ po,
+                                                            void* __restrict__ out, int P,
+                                                            long long rows)
 {
-    const size_t r = blockIdx.x;
-    const int d = threadIdx.x;
+    constexpr int LPR = D / 4;     // lanes per row
+    constexpr int RPW = 64 / LPR;  // rows per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long r = ((long long)blockIdx.x * kMergeWaves + wave) * RPW + lane / LPR;
+    if (r >= rows)
+        return;
+    const int d4 = lane % LPR;
     const float* m = pm + r * P;
     const float* l = pl + r * P;
-    const float* o = po + r * P * D + d;
+    const float4* o = (const float4*)(po + r * P * D) + d4;
     float M = -INFINITY;
     for (int c = 0; c < P; ++c)
         M = fmaxf(M, m[c]);
-    float L = 0.f, y = 0.f;
+    float L = 0.f;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
     if (M != -INFINITY) {
+#pragma unroll 8
         for (int c = 0; c < P; ++c) {
             const float mc = m[c];
+            const float4 v = o[(size_t)c * (D / 4)];
             if (mc == -INFINITY)
                 continue;  // empty chunk: weight 0
             const float e = expf(mc - M);
             L = fmaf(l[c], e, L);
-            y = fmaf(o[(size_t)c * D], e, y);
+            y.x = fmaf(v.x, e, y.x);
+            y.y = fmaf(v.y, e, y.y);
+            y.z = fmaf(v.z, e, y.z);
+            y.w = fmaf(v.w, e, y.w);
         }
     }
-    const float res = (L > 0.f) ? y / L : 0.f;
-    if constexpr (OUTF16)
-        ((_Float16*)out)[r * D + d] = (_Float16)res;
-    else
-        ((float*)out)[r * D + d] = res;
+    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (L > 0.f)
+        res = make_float4(y.x / L, y.y / L, y.z / L, y.w / L);
+    if constexpr (OUTF16) {
+        const half4_t h = {(_Float16)res.x, (_Float16)res.y, (_Float16)res.z, (_Float16)res.w};
+        *(half4_t*)((_Float16*)out + r * D + 4 * d4) = h;
+    } else {
+        *(float4*)((float*)out + r * D + 4 * d4) = res;
+    }
 }
 
 // ------------------------------------------------------------- launch ---
@@ -426,17 +446,19 @@ hipError_t launch_attend(const AttnLaunch& a, hipStream_t s)
 
 hipError_t launch_merge(const AttnLaunch& a, hipStream_t s)
 {
-    const unsigned rows = (unsigned)(a.B * a.T * a.Hq);
+    const long long rows = (long long)a.B * a.T * a.Hq;
+    const int rpb = kMergeWaves * 64 / (a.D / 4);  // rows per workgroup
+    const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
     if (a.D == 64) {
         if (a.out_f16)
-            k_merge<64, true><<<rows, 64, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P);
+            k_merge<64, true><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
         else
-            k_merge<64, false><<<rows, 64, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P);
+            k_merge<64, false><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
     } else {
         if (a.out_f16)
-            k_merge<256, true><<<rows, 256, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P);
+            k_merge<256, true><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
         else
-            k_merge<256, false><<<rows, 256, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P);
+            k_merge<256, false><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
     }
     return hipGetLastError();
 }
