@@ -39,9 +39,9 @@ CONFIGS = {
     "tiny": dict(T=1, N=512, di=64, k=128, dense_max=131, Hq=4, Hkv=1, D=64, P=4,
                  q_dtype="f32", out_dtype="f32", heavy_tail=False),
     # 1 token, 24 q heads x 256, 2 KV heads, 8192 cells, index dim 128, top-2048,
-    # 8 split-KV partials (chunks of 256 kept cells).
+    # 4 split-KV partials (chunks of 512 kept cells).
     "decode": dict(T=1, N=8192, di=128, k=2048, dense_max=2051, Hq=24, Hkv=2, D=256,
-                   P=8, q_dtype="f32", out_dtype="f32", heavy_tail=False),
+                   P=4, q_dtype="f32", out_dtype="f32", heavy_tail=False),
     # 8 draft tokens, 65536 cells, 16 partials per token.
     "draft": dict(T=8, N=65536, di=128, k=2048, dense_max=2051, Hq=24, Hkv=2, D=256,
                   P=16, q_dtype="f32", out_dtype="f32", heavy_tail=False),

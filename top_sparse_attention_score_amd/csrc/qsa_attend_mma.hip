@@ -21,8 +21,8 @@
 // fp16 products are exact in fp32, so the remaining error is fp32
 // accumulation order plus the 2^-22 split residue.
 //
-// Mapping (one wave per (token, chunk) item, four items per workgroup, KV
-// head = blockIdx.y; a tile is 32 consecutive kept cells):
+// Mapping (one wave per (token, chunk) item, four items of one KV head per
+// workgroup; a tile is 32 consecutive kept cells):
 //   QK  C[h][cell] = sum_d q[h][d] K[cell][d] per 32-element scale block;
 //       A = q (row h = lane%16, elements 8*(lane/16)..+7 of the block),
 //       B = K codes (column = cell lane%16 of a 16-cell half, the same 8
@@ -175,13 +175,13 @@ __device__ __forceinline__ void load_q_block(const void* q, size_t prow, int hq,
 // SHQ: the four waves of the workgroup are chunks of one token and share the
 // split query through LDS (requires P % 4 == 0).
 template <int G, int D, bool QF16, bool SHQ>
-__global__ __launch_bounds__(64 * kMmaWaves, SHQ ? 2 : 1) void k_attend_mma(
+__global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_attend_mma(
     const void* __restrict__ q, const int8_t* __restrict__ Kq, const uint8_t* __restrict__ Ksc,
     const int8_t* __restrict__ Vq, const uint8_t* __restrict__ Vsc, long long kq_cs,
     long long ksc_cs, long long vq_cs, long long vsc_cs, long long kq_bs, long long ksc_bs,
     long long vq_bs, long long vsc_bs, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ n_sel, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ po, int T, int Hq, int P, int cap, int N, int BT, float scale)
+    float* __restrict__ po, int T, int Hq, int Hkv, int P, int cap, int N, int BT, float scale)
 {
     static_assert(G <= 16, "one 16-row head block per KV head");
     constexpr int NB = D / 32;                // scale blocks per head row
@@ -197,16 +197,26 @@ __global__ __launch_bounds__(64 * kMmaWaves, SHQ ? 2 : 1) void k_attend_mma(
     __shared__ __align__(16) float p_all[kMmaWaves][16 * PP];
     __shared__ __align__(16) half8_t q_all[SHQ ? QH * NB * 64 : 1];
 
+    // Workgroup w serves KV head g = (w / 8) % Hkv of item group
+    // (w / (8 Hkv)) * 8 + w % 8: the groups' KV heads are 8 workgroup ids
+    // apart, so (workgroups being spread round-robin over the 8 XCDs) they
+    // run on one XCD at about the same time and share its L2 for the cache
+    // lines both heads touch (scales, ids).  The grid is padded to a
+    // multiple of 8 Hkv.
+    const int wg = blockIdx.x;
+    const int g = (wg >> 3) % Hkv;
+    const long long group = (long long)(wg / (8 * Hkv)) * 8 + (wg & 7);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long item = (long long)blockIdx.x * kMmaWaves + wave;
+    const long long item = group * kMmaWaves + wave;
     const int lane = threadIdx.x & 63;
     const int hq = lane & 15, q4 = lane >> 4;
-    const int g = blockIdx.y;
+    if (group * kMmaWaves >= (long long)BT * P)
+        return;  // grid padding (whole workgroup)
 
     if constexpr (SHQ) {
         // Every wave of the block has the same token (P % 4 == 0 and the grid
         // covers whole blocks of items); each builds some query blocks.
-        const int bt0 = (int)(((long long)blockIdx.x * kMmaWaves) / P);
+        const int bt0 = (int)((group * kMmaWaves) / P);
         const size_t prow0 = (size_t)bt0 * Hq + (size_t)g * G;
         for (int blk = wave; blk < NB; blk += kMmaWaves) {
             half8_t hi, lo;
@@ -500,11 +510,13 @@ template <int G, int D, bool QF16>
 static void launch_mma_gdq(const AttnLaunch& a, hipStream_t s)
 {
     const long long items = (long long)a.B * a.T * a.P;
-    dim3 grid((unsigned)((items + kMmaWaves - 1) / kMmaWaves), (unsigned)a.Hkv);
+    const long long groups = (items + kMmaWaves - 1) / kMmaWaves;
+    const long long per = 8LL * a.Hkv;  // workgroups per 8 groups
+    const unsigned grid = (unsigned)((groups + 7) / 8 * per);
 #define QSA_MMA_ARGS                                                                         \
     a.q, a.Kq, (const uint8_t*)a.Ksc, a.Vq, (const uint8_t*)a.Vsc, a.kq_cs, a.ksc_cs, a.vq_cs, \
         a.vsc_cs, a.kq_bs, a.ksc_bs, a.vq_bs, a.vsc_bs, a.ids, a.n_sel, a.pm, a.pl, a.po, a.T, \
-        a.Hq, a.P, a.cap, a.N, a.B * a.T, a.scale
+        a.Hq, a.Hkv, a.P, a.cap, a.N, a.B * a.T, a.scale
     if (a.P % kMmaWaves == 0)
         k_attend_mma<G, D, QF16, true><<<grid, 64 * kMmaWaves, 0, s>>>(QSA_MMA_ARGS);
     else
