@@ -68,13 +68,16 @@ def attend_flops(p: dict, n_sel_total: int) -> float:
 # Source file of each attend kernel family (its hash gates profiled traffic).
 ATTEND_SOURCES = {"matrix": "qsa_attend_mma.hip", "vector": "qsa_attend.hip"}
 ATTEND_KERNELS = {"matrix": "k_attend_mma", "vector": "k_attend"}
+# Headers whose code the attend kernels compile in (also hashed).
+ATTEND_HEADERS = ("qsa_device.h", "qsa_mma.h")
 
 
 def profiled_traffic(workload: str, B: int, P: int, algo: str):
     """HBM bytes per attend dispatch from the committed rocprofv3 summary of
     this exact launch configuration (profiles/<kernel>_<workload>_b<B>_P<P>.md),
     scaled by the copy-kernel calibration recorded there; None if there is no
-    such summary or the kernel source changed since it was taken."""
+    such summary or the kernel source (with the device headers it includes)
+    changed since it was taken."""
     import hashlib
     kern = ATTEND_KERNELS[algo]
     path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_b{B}_P{P}.md")
@@ -86,7 +89,8 @@ def profiled_traffic(workload: str, B: int, P: int, algo: str):
         if ":" in line and not line.startswith(("|", "#", "`")):
             key, _, val = line.partition(":")
             fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in [src] + [
+        os.path.join(os.path.dirname(src), h) for h in ATTEND_HEADERS])).hexdigest()[:16]
     if fields.get("traffic_source_sha256_16") != sha:
         return None
     try:

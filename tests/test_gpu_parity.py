@@ -242,3 +242,22 @@ def test_chunk_max_is_exact_max_of_logits(algo):
     whole = run_gpu(inp, P=1, algo=algo)
     assert np.all(one["pl"] == 1.0)
     assert whole["pm"][..., 0].tobytes() == one["pm"].max(axis=-1).tobytes()
+
+
+@pytest.mark.parametrize("algo", ["matrix", "vector"])
+@pytest.mark.parametrize("cfg,batch", [("decode", 2), ("draft", 1), ("tiny", 4)])
+def test_fp32_level_precision(orc, cfg, batch, algo):
+    """Both attention kernels keep fp32-level accuracy, far inside the
+    workload tolerance: fp32 accumulation of <= 2048 exact products gives a
+    relative error of order 2^-24 * sqrt(2048) ~ 3e-6, so rel-L2 <= 1e-5.
+    A lost lo half of a split fp16 operand in the matrix kernel would show
+    as ~2^-11 (5e-4) relative error and fail this."""
+    inp = make_inputs(cfg, seed=77, batch=batch)
+    say(f"[precision] {cfg} B={batch} {algo}")
+    res = run_gpu(inp, algo=algo)
+    ref = _oracle_all(orc, inp, inp["P"])
+    diff = res["out"].astype(np.float64) - ref["out"]
+    rel = np.linalg.norm(diff) / np.linalg.norm(ref["out"])
+    assert rel <= 1e-5, rel
+    fin = np.isfinite(ref["pm"])
+    assert np.abs(res["pm"].astype(np.float64)[fin] - ref["pm"][fin]).max() <= 1e-5

@@ -651,47 +651,15 @@ __device__ __forceinline__ uint32_t row_excl_scan(uint32_t v, uint32_t& total,
     return base + x - v;
 }
 
+// Selects the k largest of the row's keys, which thread t holds for cells
+// c0 = t*KPT .. c0+KPT-1 (0 for cells past the token's position), and writes
+// the kept cells in ascending order, -1 padding and the count.
 template <int KPT>
-__global__ __launch_bounds__(kRowThreads) void k_sel_row(const uint32_t* __restrict__ keys,
-                                                         int32_t* __restrict__ ids,
-                                                         int32_t* __restrict__ n_sel, int T, int N,
-                                                         int pos0, int k, int dense_max, int cap)
+__device__ __forceinline__ void select_row(const uint32_t (&key)[KPT], int c0, int k, int cap,
+                                           int32_t* __restrict__ out, int32_t* __restrict__ n_out,
+                                           uint32_t* hist, uint32_t* s_wave, uint32_t* s_pick)
 {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t s_wave[kRowThreads / 64];
-    __shared__ uint32_t s_pick[2];
-    const int row = blockIdx.x;
-    const int nvis = pos0 + (row % T) + 1;
     const int tid = threadIdx.x;
-    int32_t* out = ids + (size_t)row * cap;
-
-    if (!token_selects(nvis, k, dense_max)) {
-        // Keep every visible cell: ids 0..nvis-1, then -1.
-        if (tid == 0)
-            n_sel[row] = nvis;
-        for (int i = tid; i < cap; i += kRowThreads)
-            out[i] = (i < nvis) ? i : -1;
-        return;
-    }
-
-    const int c0 = tid * KPT;
-    const uint32_t* kr = keys + (size_t)row * N + c0;
-    uint32_t key[KPT];
-    if ((N & 3) == 0 && c0 + KPT <= nvis) {
-#pragma unroll
-        for (int j = 0; j < KPT; j += 4) {
-            const uint4 v = *(const uint4*)(kr + j);
-            key[j] = v.x;
-            key[j + 1] = v.y;
-            key[j + 2] = v.z;
-            key[j + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            key[j] = (c0 + j < nvis) ? kr[j] : 0u;
-    }
-
     // Radix select of the k-th largest key.
     uint32_t prefix = 0, pmask = 0, r = (uint32_t)k;
 #pragma unroll 1
@@ -757,7 +725,112 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_row(const uint32_t* __restr
     for (int i = k + tid; i < cap; i += kRowThreads)
         out[i] = -1;
     if (tid == 0)
-        n_sel[row] = k;
+        *n_out = k;
+}
+
+// Dense row: ids 0..nvis-1, then -1.
+__device__ __forceinline__ void dense_row(int nvis, int cap, int32_t* __restrict__ out,
+                                          int32_t* __restrict__ n_out)
+{
+    if (threadIdx.x == 0)
+        *n_out = nvis;
+    for (int i = threadIdx.x; i < cap; i += kRowThreads)
+        out[i] = (i < nvis) ? i : -1;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kRowThreads) void k_sel_row(const uint32_t* __restrict__ keys,
+                                                         int32_t* __restrict__ ids,
+                                                         int32_t* __restrict__ n_sel, int T, int N,
+                                                         int pos0, int k, int dense_max, int cap)
+{
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t s_wave[kRowThreads / 64];
+    __shared__ uint32_t s_pick[2];
+    const int row = blockIdx.x;
+    const int nvis = pos0 + (row % T) + 1;
+    int32_t* out = ids + (size_t)row * cap;
+    if (!token_selects(nvis, k, dense_max)) {
+        dense_row(nvis, cap, out, n_sel + row);
+        return;
+    }
+    const int c0 = threadIdx.x * KPT;
+    const uint32_t* kr = keys + (size_t)row * N + c0;
+    uint32_t key[KPT];
+    if ((N & 3) == 0 && c0 + KPT <= nvis) {
+#pragma unroll
+        for (int j = 0; j < KPT; j += 4) {
+            const uint4 v = *(const uint4*)(kr + j);
+            key[j] = v.x;
+            key[j + 1] = v.y;
+            key[j + 2] = v.z;
+            key[j + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            key[j] = (c0 + j < nvis) ? kr[j] : 0u;
+    }
+    select_row<KPT>(key, c0, k, cap, out, n_sel + row, hist, s_wave, s_pick);
+}
+
+// One token (T == 1) per workgroup, scan and select fused: the 1024
+// threads score the visible key rows (16 lanes per 256-byte row as in
+// k_idx_scan, eight rows in flight per lane) into an LDS key table, then
+// select from it.  Used while the row's keys fit in LDS.
+template <int DI, int KPT>
+__global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __restrict__ q_idx,
+                                                             const uint4* __restrict__ K_idx,
+                                                             int32_t* __restrict__ ids,
+                                                             int32_t* __restrict__ n_sel, int N,
+                                                             int pos0, int k, int dense_max, int cap)
+{
+    constexpr int LPR = DI / 8;                // lanes per key row
+    constexpr int RPS = kRowThreads / LPR;     // rows per block-wide step
+    constexpr int U = 16;                      // steps in flight per thread
+    __shared__ uint32_t keys_s[kRowThreads * KPT];
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t s_wave[kRowThreads / 64];
+    __shared__ uint32_t s_pick[2];
+    const int b = blockIdx.x;
+    const int nvis = pos0 + 1;
+    int32_t* out = ids + (size_t)b * cap;
+    if (!token_selects(nvis, k, dense_max)) {
+        dense_row(nvis, cap, out, n_sel + b);
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int sub = tid % LPR;
+    const uint4 qv = q_idx[(size_t)b * (DI / 8) + sub];
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+    const uint4* Kb = K_idx + (size_t)b * N * (DI / 8) + sub;
+    for (int r0 = tid / LPR; r0 < nvis; r0 += RPS * U) {
+        uint4 kv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(r0 + u * RPS, nvis - 1);
+            kv[u] = Kb[(size_t)j * (DI / 8)];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = r0 + u * RPS;
+            const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
+            acc = row_sum<LPR>(acc);
+            if (sub == 0 && j < nvis)
+                keys_s[j] = score_key(acc);
+        }
+    }
+    __syncthreads();
+    const int c0 = tid * KPT;
+    uint32_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        key[j] = (c0 + j < nvis) ? keys_s[c0 + j] : 0u;
+    select_row<KPT>(key, c0, k, cap, out, n_sel + b, hist, s_wave, s_pick);
 }
 
 // Keys per thread of the single-block select for rows of N cells (0 if a row
@@ -843,6 +916,21 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
     // Scores are needed only when some token keeps fewer cells than it sees.
     const int nvis_max = a.pos0 + a.T;  // cells visible to the last token
     const bool any_select = token_selects(nvis_max, a.k, a.dense_max);
+    if (any_select && a.T == 1 && a.N <= kRowThreads * 16) {
+        const uint4* q = (const uint4*)a.q_idx;
+        const uint4* K = (const uint4*)a.K_idx;
+#define QSA_FUSED(DI, KPT)                                                               \
+    k_scan_select<DI, KPT><<<a.B, kRowThreads, 0, s>>>(q, K, a.ids, a.n_sel, a.N, a.pos0, a.k, \
+                                                       a.dense_max, a.cap)
+        const int kpt = row_select_kpt(a.N);
+        if (a.DI == 64) {
+            if (kpt <= 4) QSA_FUSED(64, 4); else if (kpt <= 8) QSA_FUSED(64, 8); else QSA_FUSED(64, 16);
+        } else {
+            if (kpt <= 4) QSA_FUSED(128, 4); else if (kpt <= 8) QSA_FUSED(128, 8); else QSA_FUSED(128, 16);
+        }
+#undef QSA_FUSED
+        return hipGetLastError();
+    }
     if (any_select) {
         if (a.T <= 16) {
             if (a.DI == 64)
