@@ -9,15 +9,22 @@
 // Layer-Local Aliasing", section 1, Target 2).
 //
 // Kernels
-//   k_idx_scan   decode (T <= 16): streams every visible cell's fp16 key row
-//                once, 16 lanes per row (coalesced), scores it against all T
-//                tokens with v_dot2 (fp16 x fp16 products, fp32
-//                accumulation) and sums the row across its lanes with DPP.
+//   k_idx_scan   one token (T = 1): streams every visible cell's fp16 key
+//                row once, 16 lanes per row (coalesced), scores it with
+//                v_dot2 (fp16 x fp16 products, fp32 accumulation) and sums
+//                the row across its lanes with DPP.
+//   k_idx_mscan  2 <= T <= 16 (draft): the same stream, scored on MFMA
+//                (v_mfma_f32_16x16x32_f16, tokens padded to 16 rows), no
+//                cross-lane reduction.
+//   k_scan_select one token with a row of at most 16384 cells (decode):
+//                scan and select fused in one workgroup per token.
 //   k_idx_gemm   prompt chunk (T > 16): [T x d_idx] x [d_idx x N] on MFMA
 //                (v_mfma_f32_16x16x16_f16), 64 tokens x 64 cells per
 //                workgroup.
-//   k_sel_*      exact top-k over the score keys, tiled over the whole chip
-//                (histogram, filter + pivot, ordered write); see below.
+//   k_sel_row    exact top-k of rows up to 65536 cells, one workgroup per
+//                token, keys in registers.
+//   k_sel_*      exact top-k over the score keys of longer rows, tiled over
+//                the whole chip (histogram, filter + pivot, ordered write).
 #include <algorithm>
 
 #include "qsa_device.h"
@@ -94,6 +101,68 @@ __global__ __launch_bounds__(256) void k_idx_scan(const uint4* __restrict__ q_id
                 acc = row_sum<LPR>(acc);
                 if (sub == 0 && j < nvis_max)
                     keys[((size_t)b * T + t) * N + j] = score_key(acc);
+            }
+        }
+    }
+}
+
+// A few tokens (2 <= T <= 16) against every visible cell on the matrix
+// cores: a wave takes 16 consecutive cells per group; C[token][cell] =
+// sum_d q[token][d] K[cell][d] with v_mfma_f32_16x16x32_f16 (A = the T
+// index queries padded to 16 rows, B = the 16 cells' keys).  The reduction
+// index is permuted (the same way in both operands): at step s lane group g
+// supplies elements 64*(s/2) + 16*g + 8*(s%2) .. +7, so over a step pair a
+// lane reads 32 contiguous bytes and the four groups a whole 128-byte line
+// of its cell.  Every lane then holds four tokens' scores of one cell, with
+// no cross-lane reduction; on the seeded grid inputs fp32 accumulation is
+// exact in any order.  Four groups (64 cells) are in flight per wave.
+template <int DI>
+__global__ __launch_bounds__(256) void k_idx_mscan(const _Float16* __restrict__ q_idx,
+                                                   const _Float16* __restrict__ K_idx,
+                                                   uint32_t* __restrict__ keys, int T, int N,
+                                                   int nvis_max)
+{
+    typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+    constexpr int KS = DI / 32;   // MFMA steps per key row
+    constexpr int U = 4;          // 16-cell groups per wave and pass
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, q4 = lane >> 4;
+
+    // A operand: token col (zero rows beyond T), elements 32s + 8*q4 .. +7.
+    h8_t qa[KS];
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+        if (col < T)
+            qa[st] = *(const h8_t*)(q_idx + ((size_t)b * T + col) * DI + 64 * (st >> 1) +
+                                    16 * q4 + 8 * (st & 1));
+        else
+            qa[st] = h8_t{};
+    }
+    const int c0 = (blockIdx.x * 4 + wave) * (16 * U);
+    h8_t kb[U][KS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = min(c0 + 16 * u + col, nvis_max - 1);
+        const _Float16* kr = K_idx + ((size_t)b * N + j) * DI + 16 * q4;
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            kb[u][st] = *(const h8_t*)(kr + 64 * (st >> 1) + 8 * (st & 1));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], kb[u][st], acc, 0, 0, 0);
+        // lane holds tokens 4*q4 + r of cell c0 + 16u + col
+        const int j = c0 + 16 * u + col;
+        if (j < nvis_max) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * q4 + r;
+                if (t < T)
+                    keys[((size_t)b * T + t) * N + j] = score_key(acc[r]);
             }
         }
     }
@@ -678,15 +747,16 @@ __device__ __forceinline__ void select_row(const uint32_t (&key)[KPT], int c0, i
         // nb-2-2t (nb / kRowThreads = 2 or 1 bins per thread).
         const int per = nb / kRowThreads;
         const int hi = nb - 1 - tid * per;
-        uint32_t sum = 0;
+        uint32_t cnt_i[2] = {0u, 0u};
         for (int i = 0; i < per; ++i)
-            sum += hist[hi - i];
+            cnt_i[i] = hist[hi - i];
+        const uint32_t sum = cnt_i[0] + cnt_i[1];
         uint32_t total;
         const uint32_t ex = row_excl_scan(sum, total, s_wave);
         if (ex < r && r <= ex + sum) {
             uint32_t acc = ex;
             for (int i = 0; i < per; ++i) {
-                const uint32_t cnt = hist[hi - i];
+                const uint32_t cnt = cnt_i[i];
                 if (acc < r && r <= acc + cnt) {
                     s_pick[0] = (uint32_t)(hi - i);
                     s_pick[1] = acc;
@@ -886,18 +956,8 @@ static void launch_scan(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipS
 {
     constexpr int rows_per_block = (256 / (DI / 8)) * 8;
     dim3 grid((nvis_max + rows_per_block - 1) / rows_per_block, a.B);
-    const uint4* q = (const uint4*)a.q_idx;
-    const uint4* K = (const uint4*)a.K_idx;
-    if (a.T <= 1)
-        k_idx_scan<DI, 1><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
-    else if (a.T <= 2)
-        k_idx_scan<DI, 2><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
-    else if (a.T <= 4)
-        k_idx_scan<DI, 4><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
-    else if (a.T <= 8)
-        k_idx_scan<DI, 8><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
-    else
-        k_idx_scan<DI, 16><<<grid, 256, 0, s>>>(q, K, keys, a.T, a.N, nvis_max);
+    k_idx_scan<DI, 1><<<grid, 256, 0, s>>>((const uint4*)a.q_idx, (const uint4*)a.K_idx, keys,
+                                           a.T, a.N, nvis_max);
 }
 
 template <int DI>
@@ -932,11 +992,21 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
         return hipGetLastError();
     }
     if (any_select) {
-        if (a.T <= 16) {
+        if (a.T == 1) {
             if (a.DI == 64)
                 launch_scan<64>(a, w.keys, nvis_max, s);
             else
                 launch_scan<128>(a, w.keys, nvis_max, s);
+        } else if (a.T <= 16) {
+            const dim3 grid((nvis_max + 255) / 256, a.B);  // 4 waves x 64 cells
+            if (a.DI == 64)
+                k_idx_mscan<64><<<grid, 256, 0, s>>>((const _Float16*)a.q_idx,
+                                                     (const _Float16*)a.K_idx, w.keys, a.T, a.N,
+                                                     nvis_max);
+            else
+                k_idx_mscan<128><<<grid, 256, 0, s>>>((const _Float16*)a.q_idx,
+                                                      (const _Float16*)a.K_idx, w.keys, a.T, a.N,
+                                                      nvis_max);
         } else {
             if (a.DI == 64)
                 launch_gemm<64>(a, w.keys, nvis_max, s);
