@@ -341,55 +341,80 @@ __global__ __launch_bounds__(64 * kAttendWaves) void k_attend(
 
 constexpr int kMergeWaves = 4;
 
-// D/4 lanes per (token, query head) row, 4 consecutive output elements per
-// lane (float4 loads of every chunk's partial row); a wave covers 64/(D/4)
-// rows.  Per element: M = max_c m_c, then over the chunks in order
-// e = exp(m_c - M), L = fma(l_c, e, L), y = fma(o_c, e, y), and one division.
-template <int D, bool OUTF16>
+// EPL (4 or 1) consecutive output elements per lane, D/EPL lanes per (token,
+// query head) row; a wave covers 64/(D/EPL) rows (EPL = 1 spreads rows with
+// many chunks over more waves).  Per element: M = max_c m_c, then over the
+// chunks in order e = exp(m_c - M) (0 for an empty chunk), L = fma(l_c, e,
+// L), y = fma(o_c, e, y), and one division.  An empty chunk has l = o = 0,
+// so its zero weight leaves L and y bitwise unchanged.
+template <int D, int EPL, bool OUTF16>
 __global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restrict__ pm,
                                                             const float* __restrict__ pl,
                                                             const float* __restrict__ po,
                                                             void* __restrict__ out, int P,
                                                             long long rows)
 {
-    constexpr int LPR = D / 4;     // lanes per row
-    constexpr int RPW = 64 / LPR;  // rows per wave
+    constexpr int LPR = D / EPL;   // lanes per row
+    constexpr int RPW = 64 / LPR;  // rows per wave (D = 64, EPL = 1: one row per wave)
+    static_assert(LPR <= 64 || LPR % 64 == 0, "rows map to whole lane groups or waves");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const long long r = ((long long)blockIdx.x * kMergeWaves + wave) * RPW + lane / LPR;
+    long long r;
+    int de;  // first element of this lane
+    if constexpr (LPR <= 64) {
+        r = ((long long)blockIdx.x * kMergeWaves + wave) * RPW + lane / LPR;
+        de = EPL * (lane % LPR);
+    } else {
+        constexpr int WPR = LPR / 64;  // waves per row
+        r = ((long long)blockIdx.x * kMergeWaves + wave) / WPR;
+        de = EPL * (64 * (wave % WPR) + lane);
+    }
     if (r >= rows)
         return;
-    const int d4 = lane % LPR;
     const float* m = pm + r * P;
     const float* l = pl + r * P;
-    const float4* o = (const float4*)(po + r * P * D) + d4;
+    const float* o = po + r * P * D + de;
     float M = -INFINITY;
     for (int c = 0; c < P; ++c)
         M = fmaxf(M, m[c]);
     float L = 0.f;
-    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    float y[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        y[e] = 0.f;
     if (M != -INFINITY) {
 #pragma unroll 8
         for (int c = 0; c < P; ++c) {
             const float mc = m[c];
-            const float4 v = o[(size_t)c * (D / 4)];
-            if (mc == -INFINITY)
-                continue;  // empty chunk: weight 0
-            const float e = expf(mc - M);
-            L = fmaf(l[c], e, L);
-            y.x = fmaf(v.x, e, y.x);
-            y.y = fmaf(v.y, e, y.y);
-            y.z = fmaf(v.z, e, y.z);
-            y.w = fmaf(v.w, e, y.w);
+            const float w = (mc == -INFINITY) ? 0.f : expf(mc - M);
+            L = fmaf(l[c], w, L);
+            if constexpr (EPL == 4) {
+                const float4 v = *(const float4*)(o + (size_t)c * D);
+                y[0] = fmaf(v.x, w, y[0]);
+                y[1] = fmaf(v.y, w, y[1]);
+                y[2] = fmaf(v.z, w, y[2]);
+                y[3] = fmaf(v.w, w, y[3]);
+            } else {
+                y[0] = fmaf(o[(size_t)c * D], w, y[0]);
+            }
         }
     }
-    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (L > 0.f)
-        res = make_float4(y.x / L, y.y / L, y.z / L, y.w / L);
+    float res[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        res[e] = (L > 0.f) ? y[e] / L : 0.f;
     if constexpr (OUTF16) {
-        const half4_t h = {(_Float16)res.x, (_Float16)res.y, (_Float16)res.z, (_Float16)res.w};
-        *(half4_t*)((_Float16*)out + r * D + 4 * d4) = h;
+        _Float16* dst = (_Float16*)out + r * D + de;
+        if constexpr (EPL == 4)
+            *(half4_t*)dst = half4_t{(_Float16)res[0], (_Float16)res[1], (_Float16)res[2],
+                                     (_Float16)res[3]};
+        else
+            dst[0] = (_Float16)res[0];
     } else {
-        *(float4*)((float*)out + r * D + 4 * d4) = res;
+        float* dst = (float*)out + r * D + de;
+        if constexpr (EPL == 4)
+            *(float4*)dst = make_float4(res[0], res[1], res[2], res[3]);
+        else
+            dst[0] = res[0];
     }
 }
 
@@ -444,21 +469,32 @@ hipError_t launch_attend(const AttnLaunch& a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int D, int EPL>
+static void launch_merge_de(const AttnLaunch& a, long long rows, hipStream_t s)
+{
+    const long long lanes = rows * (D / EPL);
+    const unsigned grid = (unsigned)((lanes + 64 * kMergeWaves - 1) / (64 * kMergeWaves));
+    if (a.out_f16)
+        k_merge<D, EPL, true><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+    else
+        k_merge<D, EPL, false><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+}
+
 hipError_t launch_merge(const AttnLaunch& a, hipStream_t s)
 {
     const long long rows = (long long)a.B * a.T * a.Hq;
-    const int rpb = kMergeWaves * 64 / (a.D / 4);  // rows per workgroup
-    const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+    // Many chunks per row: one element per lane (four times the waves).
+    const bool wide = a.P >= 32;
     if (a.D == 64) {
-        if (a.out_f16)
-            k_merge<64, true><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+        if (wide)
+            launch_merge_de<64, 1>(a, rows, s);
         else
-            k_merge<64, false><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+            launch_merge_de<64, 4>(a, rows, s);
     } else {
-        if (a.out_f16)
-            k_merge<256, true><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+        if (wide)
+            launch_merge_de<256, 1>(a, rows, s);
         else
-            k_merge<256, false><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+            launch_merge_de<256, 4>(a, rows, s);
     }
     return hipGetLastError();
 }
