@@ -79,6 +79,10 @@ class Oracle:
         lib.qo_attend.restype = _I
         lib.qo_merge.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
         lib.qo_merge.restype = _I
+        lib.qo_quant_row.argtypes = [_I, _P, _P, _P]
+        lib.qo_quant_row.restype = _I
+        lib.qo_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
+        lib.qo_kv_append.restype = _I
         self.lib = lib
 
     # ------------------------------------------------------------- fp16 ---
@@ -169,6 +173,43 @@ class Oracle:
                 raise ValueError("oracle qo_merge rejected its arguments")
             out[b] = ob
         return out
+
+    # -------------------------------------------------------- KV append ---
+    def quant_row(self, x):
+        """One float32 row (length a multiple of 32) -> (int8 codes, fp16
+        scale bits)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        codes = np.empty(x.shape, dtype=np.int8)
+        scales = np.empty((x.size // 32,), dtype=np.uint16)
+        if self.lib.qo_quant_row(x.size, _ptr(x), _ptr(codes), _ptr(scales)) != 0:
+            raise ValueError("oracle qo_quant_row rejected its arguments")
+        return codes, scales
+
+    def kv_append(self, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, *, pos0: int):
+        """Returns copies of the dense caches (Kq, Ksc, Vq, Vsc as int8 / fp16
+        bits, K_idx as fp16 bits) with the T new tokens of every problem
+        quantised in at positions pos0 .. pos0+T-1."""
+        k_new = np.ascontiguousarray(k_new, dtype=np.float32)
+        v_new = np.ascontiguousarray(v_new, dtype=np.float32)
+        kidx_new = np.ascontiguousarray(kidx_new, dtype=np.float32)
+        B, T, Hkv, D = k_new.shape
+        di = kidx_new.shape[-1]
+        Kq, Vq = np.array(Kq, dtype=np.int8), np.array(Vq, dtype=np.int8)
+        Ksc, Vsc, K_idx = (np.array(_bits16(a)) for a in (Ksc, Vsc, K_idx))
+        N = Kq.shape[1]
+        for b in range(B):
+            kq, ks = np.ascontiguousarray(Kq[b]), np.ascontiguousarray(Ksc[b])
+            vq, vs = np.ascontiguousarray(Vq[b]), np.ascontiguousarray(Vsc[b])
+            ki = np.ascontiguousarray(K_idx[b])
+            rc = self.lib.qo_kv_append(T, N, Hkv, D, di, pos0,
+                                       _ptr(np.ascontiguousarray(k_new[b])),
+                                       _ptr(np.ascontiguousarray(v_new[b])),
+                                       _ptr(np.ascontiguousarray(kidx_new[b])),
+                                       _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), _ptr(ki))
+            if rc != 0:
+                raise ValueError("oracle qo_kv_append rejected its arguments")
+            Kq[b], Ksc[b], Vq[b], Vsc[b], K_idx[b] = kq, ks, vq, vs, ki
+        return Kq, Ksc, Vq, Vsc, K_idx
 
     # ------------------------------------------------------- whole path ---
     def run(self, inp: dict, *, P: int, scale: float | None = None):

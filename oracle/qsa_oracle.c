@@ -318,3 +318,113 @@ int qo_merge(int T, int Hq, int P, int D, const double* pm, const double* pl,
     }
     return 0;
 }
+
+/* ------------------------------------------------- KV append (quantise) --- */
+
+/*
+ * Quantisation of a new token's K or V row into the cache format: int8
+ * codes with one fp16 scale per 32 consecutive elements ([r20] section 3:
+ * int8 KV with fp16 scales; the block of 32 is the one the attention reads).
+ * The pages do not spell out the quantiser; the plain absmax reading is
+ * used, with every rounding to nearest, ties to even, on the exact values:
+ *   a = max |x| over the block,  s = fp16(a / 127),
+ *   c = clamp(round(x / s), -127, 127)   (c = 0 when s = 0).
+ * Both roundings are checked against their neighbours with exact products
+ * (an fp16 value times 127, or a code times an fp16 scale, is exact in
+ * double, and so is its difference with a float input), so the result does
+ * not depend on how double division rounds.
+ */
+
+/* Value of the binary16 pattern next to h in the direction of growing
+   magnitude (dir = +1) or shrinking magnitude (dir = -1), for h >= 0. */
+static uint16_t qo_half_step(uint16_t h, int dir)
+{
+    if (dir > 0)
+        return (uint16_t)(h < 0x7c00u ? h + 1 : h);
+    return (uint16_t)(h > 0 ? h - 1 : 0);
+}
+
+/* fp16 nearest to a / 127 for a >= 0 (ties to the even pattern). */
+static uint16_t qo_scale_of(double a)
+{
+    uint16_t h = qo_double_to_half(a / 127.0);
+    uint16_t best = h;
+    double best_err = fabs(a - 127.0 * qo_half_to_double(h));
+    for (int dir = -1; dir <= 1; dir += 2) {
+        const uint16_t g = qo_half_step(h, dir);
+        const double err = fabs(a - 127.0 * qo_half_to_double(g));
+        if (err < best_err || (err == best_err && (g & 1u) == 0 && (best & 1u) == 1)) {
+            best = g;
+            best_err = err;
+        }
+    }
+    return best;
+}
+
+/* Integer nearest to x / s for s > 0 (ties to even), clamped to +-127. */
+static int qo_code_of(double x, double s)
+{
+    const double c0 = nearbyint(x / s);
+    double best = c0, best_err = fabs(x - c0 * s);
+    for (int d = -1; d <= 1; d += 2) {
+        const double c = c0 + d;
+        const double err = fabs(x - c * s);
+        if (err < best_err || (err == best_err && fmod(fabs(c), 2.0) == 0.0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    if (best > 127.0)
+        best = 127.0;
+    if (best < -127.0)
+        best = -127.0;
+    return (int)best;
+}
+
+/* One row of n (a multiple of 32) floats -> n codes and n/32 scales. */
+int qo_quant_row(int n, const float* x, int8_t* codes, uint16_t* scales)
+{
+    if (n < 32 || n % 32)
+        return -1;
+    for (int blk = 0; blk < n / 32; ++blk) {
+        const float* xb = x + 32 * blk;
+        double a = 0.0;
+        for (int e = 0; e < 32; ++e)
+            if (fabs((double)xb[e]) > a)
+                a = fabs((double)xb[e]);
+        const uint16_t h = qo_scale_of(a);
+        const double s = qo_half_to_double(h);
+        scales[blk] = h;
+        for (int e = 0; e < 32; ++e)
+            codes[32 * blk + e] = (int8_t)(s > 0.0 ? qo_code_of((double)xb[e], s) : 0);
+    }
+    return 0;
+}
+
+/*
+ * Append T new tokens at positions pos0 .. pos0+T-1 of one problem's cache:
+ *   k_new, v_new  float [T][Hkv][D]   -> Kq, Vq int8 [N][Hkv][D] and
+ *                                        Ksc, Vsc fp16 [N][Hkv][D/32]
+ *   kidx_new      float [T][di]       -> K_idx fp16 [N][di] (nearest, ties even)
+ * Every other cell is left as it is.
+ */
+int qo_kv_append(int T, int N, int Hkv, int D, int di, int pos0, const float* k_new,
+                 const float* v_new, const float* kidx_new, int8_t* Kq, uint16_t* Ksc,
+                 int8_t* Vq, uint16_t* Vsc, uint16_t* K_idx)
+{
+    if (T < 1 || Hkv < 1 || D < 32 || D % 32 || di < 1 || pos0 < 0 || pos0 + T > N)
+        return -1;
+    for (int t = 0; t < T; ++t) {
+        const size_t cell = (size_t)(pos0 + t);
+        for (int g = 0; g < Hkv; ++g) {
+            const size_t src = ((size_t)t * Hkv + g) * D;
+            const size_t dst = (cell * Hkv + g) * D;
+            const size_t sdst = (cell * Hkv + g) * (D / 32);
+            qo_quant_row(D, k_new + src, Kq + dst, Ksc + sdst);
+            qo_quant_row(D, v_new + src, Vq + dst, Vsc + sdst);
+        }
+        for (int i = 0; i < di; ++i)
+            K_idx[cell * di + i] = qo_double_to_half((double)kidx_new[(size_t)t * di + i]);
+    }
+    return 0;
+}

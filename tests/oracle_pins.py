@@ -13,7 +13,9 @@ when it disagrees with what the pages and the mathematics fix:
 * invariants: re-associating the softmax into any number of chunks leaves the
   merged output unchanged; k >= visible cells equals dense attention;
   the kept set dominates the rest in score, ties going to lower indices;
-* hand-derived worked examples stored under tests/golden/.
+* hand-derived worked examples stored under tests/golden/;
+* the KV quantiser against exact rational arithmetic (Python fractions over
+  numpy's binary16 table), including constructed ties and subnormal scales.
 
 The same functions are run against deliberately broken copies of the oracle
 (tests/test_oracle_mutants.py) to show that each plausible mistake fails at
@@ -21,10 +23,12 @@ least one of them.
 """
 from __future__ import annotations
 
+import bisect
 import glob
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 from scipy.special import softmax
@@ -360,6 +364,118 @@ def pin_golden(orc):
                                rtol=0, atol=1e-15)
 
 
+# -------------------------------------------------------- KV quantiser ---
+
+_F16_TABLE = None
+
+
+def _f16_table():
+    """All finite non-negative binary16 values (ascending) as Fractions, with
+    their bit patterns (numpy's binary16 decoding)."""
+    global _F16_TABLE
+    if _F16_TABLE is None:
+        bits = np.arange(0, 0x7c00, dtype=np.uint32).astype(np.uint16)
+        vals = bits.view(np.float16).astype(np.float64)
+        _F16_TABLE = ([Fraction(float(v)) for v in vals], bits)
+    return _F16_TABLE
+
+
+def _exact_scale_bits(a: Fraction) -> int:
+    """Bit pattern of the binary16 value nearest to a / 127, ties to even."""
+    vals, bits = _f16_table()
+    t = a / 127
+    i = bisect.bisect_left(vals, t)
+    cands = [j for j in (i - 1, i, i + 1) if 0 <= j < len(vals)]
+    best = min(cands, key=lambda j: (abs(vals[j] - t), int(bits[j]) & 1))
+    return int(bits[best])
+
+
+def _exact_quant(x: np.ndarray):
+    """Reference quantisation of one float32 row: per 32-block absmax scale
+    fp16(a / 127) and codes round(x / s) (ties to even) clamped to +-127."""
+    codes = np.zeros(x.size, dtype=np.int8)
+    scales = np.zeros(x.size // 32, dtype=np.uint16)
+    vals, _ = _f16_table()
+    for blk in range(x.size // 32):
+        xb = [Fraction(float(v)) for v in x[32 * blk: 32 * blk + 32]]
+        a = max(abs(v) for v in xb)
+        hb = _exact_scale_bits(a)
+        scales[blk] = hb
+        sv = vals[hb]
+        for e, v in enumerate(xb):
+            c = round(v / sv) if sv != 0 else 0       # Fraction rounds half to even
+            codes[32 * blk + e] = max(-127, min(127, c))
+    return codes, scales
+
+
+def pin_quantiser_exact(orc):
+    """Codes and scales of random rows at magnitudes from fp16-subnormal
+    scales (where the +-127 clamp engages) to large ones equal the exact
+    rational reference."""
+    rng = np.random.default_rng(71)
+    for mag in (3e-9, 2e-7, 1e-4, 1.0, 37.0, 3e5):
+        for _ in range(3):
+            x = (rng.normal(size=64) * mag).astype(np.float32)
+            x[rng.integers(0, 64, 3)] = 0.0
+            got_c, got_s = orc.quant_row(x)
+            ref_c, ref_s = _exact_quant(x)
+            assert np.array_equal(got_s, ref_s), (mag, got_s, ref_s)
+            assert np.array_equal(got_c, ref_c), mag
+    # an all-zero block: scale 0, codes 0
+    c, s_ = orc.quant_row(np.zeros(32, dtype=np.float32))
+    assert not c.any() and not s_.any()
+
+
+def pin_quantiser_ties(orc):
+    """Exact ties x / s = n + 1/2 go to the even code, for both signs; the
+    block maximum 127 * s gives code +-127 and scale s exactly."""
+    for s in (0.5, 2.0 ** -10, 3.0, 0.0625 * 3):
+        x = np.zeros(32, dtype=np.float32)
+        x[0] = 127 * s
+        halves = [0.5, 1.5, 2.5, 3.5, 10.5, 125.5]
+        for i, hv in enumerate(halves):
+            x[1 + i] = hv * s
+            x[1 + len(halves) + i] = -hv * s
+        c, sc = orc.quant_row(x)
+        assert float(np.array([sc[0]], np.uint16).view(np.float16)[0]) == s
+        assert c[0] == 127
+        for i, hv in enumerate(halves):
+            lo = int(math.floor(hv))
+            even = lo if lo % 2 == 0 else lo + 1
+            assert c[1 + i] == even, (s, hv, c[1 + i])
+            assert c[1 + len(halves) + i] == -even, (s, -hv)
+
+
+def pin_append_placement(orc):
+    """kv_append writes exactly cells pos0 .. pos0+T-1: K and V rows are the
+    per-row quantisation of the new rows, index keys are numpy's binary16
+    rounding, every other cell is untouched."""
+    rng = np.random.default_rng(73)
+    B, N, T, Hkv, D, di, pos0 = 2, 12, 3, 2, 64, 16, 5
+    Kq = rng.integers(-127, 128, size=(B, N, Hkv, D)).astype(np.int8)
+    Vq = rng.integers(-127, 128, size=(B, N, Hkv, D)).astype(np.int8)
+    Ksc = rng.integers(0, 0x7000, size=(B, N, Hkv, D // 32)).astype(np.uint16)
+    Vsc = rng.integers(0, 0x7000, size=(B, N, Hkv, D // 32)).astype(np.uint16)
+    Kix = rng.integers(0, 0x7000, size=(B, N, di)).astype(np.uint16)
+    k_new = rng.normal(size=(B, T, Hkv, D)).astype(np.float32)
+    v_new = (rng.normal(size=(B, T, Hkv, D)) * 5).astype(np.float32)
+    i_new = rng.normal(size=(B, T, di)).astype(np.float32)
+    oK, oKs, oV, oVs, oI = orc.kv_append(k_new, v_new, i_new, Kq, Ksc, Vq, Vsc, Kix,
+                                         pos0=pos0)
+    keep = np.ones(N, bool)
+    keep[pos0:pos0 + T] = False
+    for a, o in ((Kq, oK), (Ksc, oKs), (Vq, oV), (Vsc, oVs), (Kix, oI)):
+        assert np.array_equal(np.asarray(a)[:, keep], np.asarray(o)[:, keep])
+    for b in range(B):
+        for t in range(T):
+            assert np.array_equal(oI[b, pos0 + t], i_new[b, t].astype(np.float16).view(np.uint16))
+            for g in range(Hkv):
+                for new, codes, scales in ((k_new, oK, oKs), (v_new, oV, oVs)):
+                    rc, rs = _exact_quant(new[b, t, g])
+                    assert np.array_equal(codes[b, pos0 + t, g], rc)
+                    assert np.array_equal(scales[b, pos0 + t, g], rs)
+
+
 ALL_PINS = [
     pin_half_decode_exhaustive,
     pin_half_encode,
@@ -373,4 +489,7 @@ ALL_PINS = [
     pin_split_invariance,
     pin_merge_textbook,
     pin_golden,
+    pin_quantiser_exact,
+    pin_quantiser_ties,
+    pin_append_placement,
 ]

@@ -69,6 +69,24 @@ MUTANTS = [
     ("k_not_clamped",
      "n = (k < nvis) ? k : nvis;",
      "n = k;"),
+    ("quant_scale_over_128",
+     "uint16_t h = qo_double_to_half(a / 127.0);",
+     "uint16_t h = qo_double_to_half(a / 128.0);"),
+    ("quant_ties_to_odd",
+     "(err == best_err && fmod(fabs(c), 2.0) == 0.0)",
+     "(err == best_err && fmod(fabs(c), 2.0) == 1.0)"),
+    ("quant_no_clamp",
+     "if (best > 127.0)\n        best = 127.0;",
+     "if (best > 128.0)\n        best = 127.0;"),
+    ("quant_absmax_first_element",
+     "if (fabs((double)xb[e]) > a)",
+     "if (e == 0)"),
+    ("append_index_key_truncated",
+     "K_idx[cell * di + i] = qo_double_to_half((double)kidx_new[(size_t)t * di + i]);",
+     "K_idx[cell * di + i] = qo_double_to_half(trunc(ldexp((double)kidx_new[(size_t)t * di + i], 8)) / 256.0);"),
+    ("append_wrong_cell",
+     "const size_t cell = (size_t)(pos0 + t);",
+     "const size_t cell = (size_t)(pos0 + t + 1 < N ? pos0 + t + 1 : pos0 + t);"),
     ("max_not_subtracted_last_chunk_only",
      "for (int c = 0; c < P; ++c)\n            if (m[c] > M)",
      "for (int c = 0; c + 1 < P; ++c)\n            if (m[c] > M)"),
