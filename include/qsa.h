@@ -209,6 +209,53 @@ QSA_API int qsa_attend(const qsa_attn_desc* desc, const void* q, const int8_t* K
 QSA_API int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* out,
               void* stream);
 
+/* ------------------------------------------------------------------------
+ * qsa_kv_append -- write T new tokens into the cache, the step that feeds
+ * the path: their K and V rows become int8 codes with one fp16 scale per
+ * 32 elements (the cache format of the "opus r20 ..." page, section 3:
+ * random int8 KV with fp16 scales) and their index keys become fp16.
+ *
+ * The pages do not spell out the quantiser; the plain absmax reading is
+ * used.  For every block of 32 consecutive elements x of a (token, KV head)
+ * row:
+ *   a = max |x|,  s = fp16(a / 127)  (saturating at 65504),
+ *   c = clamp(round(x / s), -127, 127),  c = 0 when s = 0,
+ * where both roundings are to nearest, ties to even, of the exact values
+ * (the library decides each against its neighbours with exact products).
+ * Index keys: fp16(x), to nearest, ties to even.  The results equal the
+ * oracle's bit for bit.
+ *
+ * Token t of problem b goes to cell pos0 + t; no other cell is written.
+ * Inputs (finite values)
+ *   k_new, v_new  fp32 [B][T][Hkv][D], 16-byte aligned
+ *   kidx_new      fp32 [B][T][d_idx], 16-byte aligned, or NULL (index keys
+ *                 are then not written)
+ * Outputs (the cache, in the layouts and strides qsa_attend reads: zero
+ * strides select the dense defaults [B][N][Hkv][D] and [B][N][Hkv][D/32])
+ *   Kq, Vq        int8 codes;  Ksc, Vsc  fp16 scales
+ *   K_idx         fp16 [B][N][d_idx] (ignored when kidx_new is NULL)
+ * Supported: D a multiple of 32 up to 1024; d_idx a multiple of 4;
+ * 0 <= pos0, pos0 + T <= n_cells; batch*T*Hkv*D/32 <= 2^30; code pointers
+ * and batch strides 16-byte aligned, code cell strides multiples of 16,
+ * scale pointers 2-byte aligned and scale strides even.
+ * --------------------------------------------------------------------- */
+typedef struct qsa_append_desc {
+    int batch;           /* B */
+    int T;               /* new tokens per problem */
+    int n_cells;         /* N, cells per problem */
+    int pos0;            /* cell of token 0 */
+    int Hkv;             /* KV heads */
+    int D;               /* head dimension */
+    int d_idx;           /* index key dimension */
+    int reserved;        /* must be 0 */
+    long long kq_cell_stride, ksc_cell_stride, vq_cell_stride, vsc_cell_stride;
+    long long kq_batch_stride, ksc_batch_stride, vq_batch_stride, vsc_batch_stride;
+} qsa_append_desc;
+
+QSA_API int qsa_kv_append(const qsa_append_desc* desc, const float* k_new, const float* v_new,
+                          const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc,
+                          void* K_idx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("qsa_index_topk", "qsa_attend", "qsa_merge", "qsa_index_topk_workspace",
-              "qsa_partials_floats", "qsa_status_string", "qsa_version"):
+              "qsa_partials_floats", "qsa_status_string", "qsa_version", "qsa_kv_append"):
         assert n in names
 
 
@@ -52,10 +52,13 @@ def test_version_and_status_strings():
 def test_struct_layout_matches_c(tmp_path):
     fields_i = [f[0] for f in qb.IndexDesc._fields_]
     fields_a = [f[0] for f in qb.AttnDesc._fields_]
+    fields_p = [f[0] for f in qb.AppendDesc._fields_]
     src = ["#include <stdio.h>", "#include <stddef.h>", '#include "qsa.h"', "int main(void){",
-           'printf("%zu %zu\\n", sizeof(qsa_index_desc), sizeof(qsa_attn_desc));']
+           'printf("%zu %zu %zu\\n", sizeof(qsa_index_desc), sizeof(qsa_attn_desc), '
+           'sizeof(qsa_append_desc));']
     src += [f'printf("%zu\\n", offsetof(qsa_index_desc, {f}));' for f in fields_i]
     src += [f'printf("%zu\\n", offsetof(qsa_attn_desc, {f}));' for f in fields_a]
+    src += [f'printf("%zu\\n", offsetof(qsa_append_desc, {f}));' for f in fields_p]
     src += ["return 0;}"]
     c = tmp_path / "layout.c"
     c.write_text("\n".join(src))
@@ -66,9 +69,11 @@ def test_struct_layout_matches_c(tmp_path):
                                            check=True).stdout.split()]
     assert vals[0] == ctypes.sizeof(qb.IndexDesc)
     assert vals[1] == ctypes.sizeof(qb.AttnDesc)
-    offs = vals[2:]
+    assert vals[2] == ctypes.sizeof(qb.AppendDesc)
+    offs = vals[3:]
     exp = [getattr(qb.IndexDesc, f).offset for f in fields_i] + \
-          [getattr(qb.AttnDesc, f).offset for f in fields_a]
+          [getattr(qb.AttnDesc, f).offset for f in fields_a] + \
+          [getattr(qb.AppendDesc, f).offset for f in fields_p]
     assert offs == exp
 
 
@@ -150,3 +155,35 @@ def test_null_descriptor():
     assert L.qsa_index_topk(None, 16, 16, 16, 16, 16, 64, None) == INVALID
     assert L.qsa_attend(None, 16, 16, 16, 16, 16, 16, 16, 16, None) == INVALID
     assert L.qsa_merge(None, 16, 16, None) == INVALID
+
+
+def _pdesc(**kw):
+    base = dict(batch=2, T=1, n_cells=64, pos0=10, Hkv=2, D=256, d_idx=128)
+    base.update(kw)
+    strides = base.pop("strides", None)
+    return qsa.append_desc(strides=strides, **base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), INVALID), (dict(T=0), INVALID), (dict(pos0=-1), INVALID),
+    (dict(pos0=64), INVALID), (dict(T=3, pos0=62), INVALID), (dict(D=48), INVALID),
+    (dict(D=2048), UNSUPPORTED), (dict(d_idx=6), INVALID), (dict(Hkv=0), INVALID),
+    (dict(strides=dict(kq_cell_stride=520)), INVALID),
+    (dict(strides=dict(vsc_cell_stride=33)), INVALID),
+])
+def test_append_desc_rejected(kw, code):
+    d = _pdesc(**kw)
+    L = qb.lib()
+    assert L.qsa_kv_append(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 16, 16, None) == code
+
+
+def test_append_pointer_checks():
+    L = qb.lib()
+    d = _pdesc()
+    assert L.qsa_kv_append(ctypes.byref(d), None, 16, 16, 16, 16, 16, 16, 16, None) == INVALID
+    assert L.qsa_kv_append(ctypes.byref(d), 8, 16, 16, 16, 16, 16, 16, 16, None) == INVALID
+    assert L.qsa_kv_append(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 16, None, None) == INVALID
+    assert L.qsa_kv_append(ctypes.byref(d), 16, 16, 16, 16, 1, 16, 16, 16, None) == INVALID
+    d.reserved = 1
+    assert L.qsa_kv_append(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 16, 16, None) == INVALID
+    assert L.qsa_kv_append(None, 16, 16, 16, 16, 16, 16, 16, 16, None) == INVALID

@@ -5,6 +5,7 @@ The computation lives in libqsa.so (hand-written HIP for gfx950, C ABI in
 include/qsa.h); ``qsa`` is the ctypes binding.
 """
 from .qsa import (QSA_ATTEND_AUTO, QSA_ATTEND_MATRIX, QSA_ATTEND_VECTOR,  # noqa: F401
-                  QSA_F16, QSA_F32, AttnDesc, IndexDesc, QsaError, QsaPath,  # noqa: F401
-                  attn_desc, index_desc, path_for, qsa_attend, qsa_index_topk,
+                  QSA_F16, QSA_F32, AppendDesc, AttnDesc, IndexDesc, QsaError,  # noqa: F401
+                  QsaPath, append_desc, attn_desc, index_desc, path_for, qsa_attend,
+                  qsa_index_topk, qsa_kv_append,
                   qsa_index_topk_workspace, qsa_merge, qsa_partials_floats, to_device)

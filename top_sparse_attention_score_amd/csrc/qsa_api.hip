@@ -208,4 +208,64 @@ int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* out, void*
     return QSA_OK;
 }
 
+int qsa_kv_append(const qsa_append_desc* d, const float* k_new, const float* v_new,
+                  const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc,
+                  void* K_idx, void* stream)
+{
+    if (!d)
+        return QSA_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->T < 1 || d->n_cells < 1 || d->pos0 < 0 || d->Hkv < 1 ||
+        d->D < 32 || d->D % 32 || d->reserved != 0)
+        return QSA_ERR_INVALID_ARG;
+    if ((long long)d->pos0 + d->T > d->n_cells)
+        return QSA_ERR_INVALID_ARG;
+    if (d->D > 1024)
+        return QSA_ERR_UNSUPPORTED;
+    if (kidx_new && (d->d_idx < 4 || d->d_idx % 4))
+        return QSA_ERR_INVALID_ARG;
+    if ((long long)d->batch * d->T * d->Hkv * (d->D / 32) > (1LL << 30))
+        return QSA_ERR_UNSUPPORTED;
+    if (!k_new || !v_new || !Kq || !Ksc || !Vq || !Vsc || (kidx_new && !K_idx))
+        return QSA_ERR_INVALID_ARG;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || (kidx_new && !aligned(kidx_new, 16)) ||
+        !aligned(Kq, 16) || !aligned(Vq, 16) || !aligned(Ksc, 2) || !aligned(Vsc, 2) ||
+        (kidx_new && !aligned(K_idx, 8)))
+        return QSA_ERR_INVALID_ARG;
+    qsa::AppendLaunch a;
+    const long long row = (long long)d->Hkv * d->D;
+    const long long srow = (long long)d->Hkv * (d->D / 32) * 2;
+    a.kq_cs = d->kq_cell_stride ? d->kq_cell_stride : row;
+    a.vq_cs = d->vq_cell_stride ? d->vq_cell_stride : row;
+    a.ksc_cs = d->ksc_cell_stride ? d->ksc_cell_stride : srow;
+    a.vsc_cs = d->vsc_cell_stride ? d->vsc_cell_stride : srow;
+    a.kq_bs = d->kq_batch_stride ? d->kq_batch_stride : a.kq_cs * d->n_cells;
+    a.vq_bs = d->vq_batch_stride ? d->vq_batch_stride : a.vq_cs * d->n_cells;
+    a.ksc_bs = d->ksc_batch_stride ? d->ksc_batch_stride : a.ksc_cs * d->n_cells;
+    a.vsc_bs = d->vsc_batch_stride ? d->vsc_batch_stride : a.vsc_cs * d->n_cells;
+    if (a.kq_cs < 0 || a.vq_cs < 0 || a.ksc_cs < 0 || a.vsc_cs < 0 || a.kq_bs < 0 ||
+        a.vq_bs < 0 || a.ksc_bs < 0 || a.vsc_bs < 0)
+        return QSA_ERR_INVALID_ARG;
+    if (a.kq_cs % 16 || a.vq_cs % 16 || a.kq_bs % 16 || a.vq_bs % 16 || a.ksc_cs % 2 ||
+        a.vsc_cs % 2 || a.ksc_bs % 2 || a.vsc_bs % 2)
+        return QSA_ERR_INVALID_ARG;
+    a.B = d->batch;
+    a.T = d->T;
+    a.N = d->n_cells;
+    a.pos0 = d->pos0;
+    a.Hkv = d->Hkv;
+    a.D = d->D;
+    a.DI = d->d_idx;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.kidx_new = kidx_new;
+    a.Kq = Kq;
+    a.Ksc = (uint16_t*)Ksc;
+    a.Vq = Vq;
+    a.Vsc = (uint16_t*)Vsc;
+    a.K_idx = (uint16_t*)K_idx;
+    if (qsa::launch_kv_append(a, (hipStream_t)stream) != hipSuccess)
+        return QSA_ERR_HIP;
+    return QSA_OK;
+}
+
 }  // extern "C"

@@ -49,6 +49,22 @@ struct AttnLaunch {
 // True if a kernel variant exists for (G, D, q dtype).
 bool attend_supported(int G, int D);
 
+struct AppendLaunch {
+    int B, T, N, pos0, Hkv, D, DI;
+    const float* k_new;
+    const float* v_new;
+    const float* kidx_new;  // may be null
+    int8_t* Kq;
+    uint16_t* Ksc;
+    int8_t* Vq;
+    uint16_t* Vsc;
+    uint16_t* K_idx;
+    long long kq_cs, ksc_cs, vq_cs, vsc_cs;  // cell strides, bytes
+    long long kq_bs, ksc_bs, vq_bs, vsc_bs;  // batch strides, bytes
+};
+
+hipError_t launch_kv_append(const AppendLaunch& a, hipStream_t s);
+
 hipError_t launch_attend(const AttnLaunch& a, hipStream_t s);
 // Matrix-core attend kernel (qsa_attend_mma.hip); false if no variant fits.
 bool launch_attend_mma(const AttnLaunch& a, hipStream_t s);

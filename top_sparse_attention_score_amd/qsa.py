@@ -46,6 +46,15 @@ class AttnDesc(ctypes.Structure):
                 ("vq_batch_stride", _c_ll), ("vsc_batch_stride", _c_ll)]
 
 
+class AppendDesc(ctypes.Structure):
+    _fields_ = [("batch", _c_int), ("T", _c_int), ("n_cells", _c_int), ("pos0", _c_int),
+                ("Hkv", _c_int), ("D", _c_int), ("d_idx", _c_int), ("reserved", _c_int),
+                ("kq_cell_stride", _c_ll), ("ksc_cell_stride", _c_ll),
+                ("vq_cell_stride", _c_ll), ("vsc_cell_stride", _c_ll),
+                ("kq_batch_stride", _c_ll), ("ksc_batch_stride", _c_ll),
+                ("vq_batch_stride", _c_ll), ("vsc_batch_stride", _c_ll)]
+
+
 _lib = None
 
 
@@ -72,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.qsa_attend.restype = _c_int
         L.qsa_merge.argtypes = [ctypes.POINTER(AttnDesc), _vp, _vp, _vp]
         L.qsa_merge.restype = _c_int
+        L.qsa_kv_append.argtypes = [ctypes.POINTER(AppendDesc), _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _vp]
+        L.qsa_kv_append.restype = _c_int
         _lib = L
     return _lib
 
@@ -117,6 +129,15 @@ def attn_desc(*, batch: int, T: int, Hq: int, Hkv: int, D: int, P: int, ids_cap:
     return d
 
 
+def append_desc(*, batch: int, T: int, n_cells: int, pos0: int, Hkv: int, D: int, d_idx: int,
+                strides: dict | None = None) -> AppendDesc:
+    """KV-append descriptor; `strides` as for attn_desc."""
+    d = AppendDesc(batch, T, n_cells, pos0, Hkv, D, d_idx, 0)
+    for key, val in (strides or {}).items():
+        setattr(d, key, int(val))
+    return d
+
+
 def qsa_index_topk_workspace(desc: IndexDesc) -> int:
     return int(lib().qsa_index_topk_workspace(ctypes.byref(desc)))
 
@@ -143,6 +164,13 @@ def qsa_attend(desc: AttnDesc, q, Kq, Ksc, Vq, Vsc, ids, n_sel, partials,
 def qsa_merge(desc: AttnDesc, partials, out, stream=None) -> None:
     _check(lib().qsa_merge(ctypes.byref(desc), _ptr(partials), _ptr(out), _stream(stream)),
            "qsa_merge")
+
+
+def qsa_kv_append(desc: AppendDesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
+                  stream=None) -> None:
+    _check(lib().qsa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(kidx_new),
+                               _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc), _ptr(K_idx),
+                               _stream(stream)), "qsa_kv_append")
 
 
 # ------------------------------------------------------- whole-path plan ---
