@@ -1,7 +1,9 @@
 """Throughput benchmark of the QSA hot path on one MI355X.
 
-One step = qsa_index_topk -> qsa_attend -> qsa_merge over a batch of B
-independent problems (seeded synthetic caches already resident in HBM).
+One step = qsa_kv_append -> qsa_index_topk -> qsa_attend -> qsa_merge over
+a batch of B independent problems (seeded synthetic caches already resident
+in HBM): the step's T new tokens are quantised into their cells of the
+cache, then selected from and attended to.
 The default workload is the decode step (1 token, 24 x 256 query heads,
 2 KV heads, 8192 cached cells, index dim 128, top-2048) over B = 256
 independent caches, so the working set (~2.7 GB) is far larger than the
@@ -45,10 +47,13 @@ WORKLOADS = {
 
 
 def algorithmic_bytes(p: dict, B: int, n_sel_total: int) -> dict:
-    """Bytes the method must move per step (no reuse across tokens):
-    index keys of every visible cell once per call (when any token selects),
-    the kept cells' K/V codes and scales once per token, q, ids, output."""
+    """Bytes the method must move per step (no reuse across tokens): the new
+    tokens' fp32 K/V/index rows in and their codes, scales and fp16 index
+    keys out; index keys of every visible cell once per call (when any token
+    selects); the kept cells' K/V codes and scales once per token, q, ids,
+    output."""
     T, N, di, Hq, Hkv, D, k = p["T"], p["N"], p["di"], p["Hq"], p["Hkv"], p["D"], p["k"]
+    append = B * T * (2 * Hkv * D * 4 + di * 4 + 2 * Hkv * (D + (D // 32) * 2) + di * 2)
     pos0 = p.get("pos0", N - T)
     nvis_max = pos0 + T
     qbytes = 2 if p["q_dtype"] == "f16" else 4
@@ -58,7 +63,8 @@ def algorithmic_bytes(p: dict, B: int, n_sel_total: int) -> dict:
     per_cell = Hkv * (D + (D // 32) * 2) * 2          # K and V codes + scales
     attend = n_sel_total * (per_cell + 4) + B * T * Hq * D * qbytes
     out = B * T * Hq * D * obytes
-    return dict(index=index, attend=attend, out=out, total=index + attend + out)
+    return dict(append=append, index=index, attend=attend, out=out,
+                total=append + index + attend + out)
 
 
 def attend_flops(p: dict, n_sel_total: int) -> float:
@@ -170,6 +176,18 @@ def main() -> None:
     inp["batch"] = B
     algo_code = qsa.QSA_ATTEND_MATRIX if args.algo == "matrix" else qsa.QSA_ATTEND_VECTOR
     path = qsa.path_for(inp, P=P, algo=algo_code)
+    # The step's new tokens (fp32 K / V / index rows, seeded) and their append.
+    gen = torch.Generator(device="cuda").manual_seed(4321)
+    T_new = inp["T"]
+    k_new = torch.randn((B, T_new, inp["Hkv"], inp["D"]), generator=gen, device="cuda")
+    v_new = torch.randn((B, T_new, inp["Hkv"], inp["D"]), generator=gen, device="cuda")
+    i_new = torch.randn((B, T_new, inp["di"]), generator=gen, device="cuda")
+    adesc = qsa.append_desc(batch=B, T=T_new, n_cells=inp["N"], pos0=inp["pos0"],
+                            Hkv=inp["Hkv"], D=inp["D"], d_idx=inp["di"])
+
+    def append():
+        qsa.qsa_kv_append(adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"], dev["Vq"],
+                          dev["Vsc"], dev["K_idx"])
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 18        # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -183,27 +201,30 @@ def main() -> None:
     stream = torch.cuda.current_stream()
     K, W = args.steps, args.warmup
     for _ in range(W):
+        append()
         path.run(dev)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     t_start = time.perf_counter()
     for s in range(K):
         e = evs[s]
         e[0].record(stream)
-        path.index(dev["q_idx"], dev["K_idx"])
+        append()
         e[1].record(stream)
-        path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"])
+        path.index(dev["q_idx"], dev["K_idx"])
         e[2].record(stream)
-        path.merge()
+        path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"])
         e[3].record(stream)
+        path.merge()
+        e[4].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    stage = np.zeros(3)
+    stage = np.zeros(4)
     for e in evs:
-        for i in range(3):
+        for i in range(4):
             stage[i] += e[i].elapsed_time(e[i + 1])
     stage_ms = stage / K
-    step_ms = float(evs[0][0].elapsed_time(evs[-1][3])) / K
+    step_ms = float(evs[0][0].elapsed_time(evs[-1][4])) / K
 
     n_sel_total = int(path.n_sel.sum().item())
     by = algorithmic_bytes(inp, B, n_sel_total)
@@ -212,27 +233,28 @@ def main() -> None:
     gbs = by["total"] / (step_ms * 1e-3) / 1e9
 
     # Dominant kernel: the stage with the largest average time.
-    names = ["index_topk", "attend", "merge"]
+    names = ["kv_append", "index_topk", "attend", "merge"]
     dom = int(np.argmax(stage_ms))
+    att_ms = stage_ms[2]
     if names[dom] == "attend" and args.algo == "vector":
-        achieved = flops / (stage_ms[1] * 1e-3) / 1e12
+        achieved = flops / (att_ms * 1e-3) / 1e12
         roof = dict(kernel="k_attend", bound="alu", achieved=round(achieved, 2),
                     peak=round(FP32_VALU_PEAK_TFLOPS, 1), unit="TFLOP/s",
                     frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4),
                     traffic=profiled_traffic(args.workload, B, P, args.algo),
                     algorithmic_bytes=by["attend"],
-                    hbm_gbs=round(by["attend"] / (stage_ms[1] * 1e-3) / 1e9, 1))
+                    hbm_gbs=round(by["attend"] / (att_ms * 1e-3) / 1e9, 1))
     elif names[dom] == "attend":
         # Matrix kernel: the products run on the matrix cores far below
         # their peak; the gathers of the kept cells bound it.
-        achieved = by["attend"] / (stage_ms[1] * 1e-3) / 1e9
+        achieved = by["attend"] / (att_ms * 1e-3) / 1e9
         roof = dict(kernel="k_attend_mma", bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                     traffic=profiled_traffic(args.workload, B, P, args.algo),
                     algorithmic_bytes=by["attend"],
-                    definition_tflops=round(flops / (stage_ms[1] * 1e-3) / 1e12, 2))
+                    definition_tflops=round(flops / (att_ms * 1e-3) / 1e12, 2))
     else:
-        sb = by["index"] if names[dom] == "index_topk" else by["out"]
+        sb = {"index_topk": by["index"], "merge": by["out"], "kv_append": by["append"]}[names[dom]]
         achieved = sb / (stage_ms[dom] * 1e-3) / 1e9
         roof = dict(kernel=names[dom], bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),

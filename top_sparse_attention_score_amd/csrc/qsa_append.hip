@@ -13,8 +13,8 @@
 // the smallest distance of a float / fp16 quotient to a half-integer, so
 // rounding it to the nearest even integer gives the exact decision.
 //
-// One thread per 32-element block of K or V (32 floats in, 32 codes and a
-// scale out) and one per 4 index-key elements.
+// Eight lanes per 32-element block of K or V (4 floats in, 4 codes out each;
+// the scale is written by the first) and one lane per 4 index-key elements.
 #include <math.h>
 
 #include "qsa_device.h"
@@ -56,65 +56,72 @@ __device__ __forceinline__ uint16_t scale_bits(float a)
     return best;
 }
 
-__global__ __launch_bounds__(256) void k_kv_append(AppendLaunch a, long long n_quant,
-                                                   long long n_idx)
+// Items: 8 lanes per 32-element block of K or V (4 elements each; the
+// block maximum is combined over the 8 consecutive lanes), then one lane per
+// 4 index-key elements.  Blocks occupy whole 8-lane groups, so the shuffles
+// stay inside a group.
+__global__ __launch_bounds__(256) void k_kv_append(AppendLaunch a, long long q_lanes,
+                                                   long long n_quant, long long n_idx)
 {
     const int NB = a.D / 32;
-    const long long total = n_quant + n_idx;
-    for (long long w = (long long)blockIdx.x * blockDim.x + threadIdx.x; w < total;
-         w += (long long)gridDim.x * blockDim.x) {
-        if (w < n_quant) {
-            // w = (((b * T + t) * Hkv + g) * NB + blk) * 2 + which
-            const int which = (int)(w & 1);
-            long long r = w >> 1;
+    const long long total = n_quant + n_idx;  // n_quant: q_lanes rounded up to 256
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long w0 = (long long)blockIdx.x * blockDim.x; w0 < total; w0 += stride) {
+        const long long w = w0 + threadIdx.x;
+        if (w0 < n_quant) {
+            // The whole workgroup is in the quantisation range (n_quant is a
+            // multiple of 256), so every lane reaches the shuffles.
+            // w = ((((b * T + t) * Hkv + g) * NB + blk) * 2 + which) * 8 + sub
+            const int sub = (int)(w & 7);
+            long long r = w >> 3;
+            const int which = (int)(r & 1);
+            r >>= 1;
             const int blk = (int)(r % NB);
             r /= NB;
             const int g = (int)(r % a.Hkv);
             r /= a.Hkv;
             const int t = (int)(r % a.T);
             const int b = (int)(r / a.T);
-            const float* src = (which ? a.v_new : a.k_new) +
-                               (((size_t)b * a.T + t) * a.Hkv + g) * a.D + 32 * blk;
-            float x[32];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 v = ((const float4*)src)[i];
-                x[4 * i] = v.x;
-                x[4 * i + 1] = v.y;
-                x[4 * i + 2] = v.z;
-                x[4 * i + 3] = v.w;
+            const bool live = w < q_lanes;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (live) {
+                const float* src = (which ? a.v_new : a.k_new) +
+                                   (((size_t)b * a.T + t) * a.Hkv + g) * a.D + 32 * blk + 4 * sub;
+                v = *(const float4*)src;
             }
-            float amax = 0.f;
+            float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
-            for (int e = 0; e < 32; ++e)
-                amax = fmaxf(amax, fabsf(x[e]));
+            for (int o = 1; o < 8; o <<= 1)
+                amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+            if (!live)
+                continue;
             const uint16_t sb = scale_bits(amax);
             const double s = (double)half_bits_to_float(sb);
-            uint32_t word[8];
+            const float x[4] = {v.x, v.y, v.z, v.w};
+            uint32_t word = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint32_t wv = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    int c = 0;
-                    if (s > 0.0) {
-                        const double qv = rint((double)x[4 * i + e] / s);
-                        c = (int)fmin(fmax(qv, -127.0), 127.0);
-                    }
-                    wv |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * e);
+            for (int e = 0; e < 4; ++e) {
+                int c = 0;
+                if (s > 0.0) {
+                    const double qv = rint((double)x[e] / s);
+                    c = (int)fmin(fmax(qv, -127.0), 127.0);
                 }
-                word[i] = wv;
+                word |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * e);
             }
             const long long cell = (long long)(a.pos0 + t);
             int8_t* codes = (which ? a.Vq : a.Kq) + (long long)b * (which ? a.vq_bs : a.kq_bs) +
-                            cell * (which ? a.vq_cs : a.kq_cs) + (long long)g * a.D + 32 * blk;
-            ((uint4*)codes)[0] = make_uint4(word[0], word[1], word[2], word[3]);
-            ((uint4*)codes)[1] = make_uint4(word[4], word[5], word[6], word[7]);
-            char* sc = (char*)(which ? a.Vsc : a.Ksc) + (long long)b * (which ? a.vsc_bs : a.ksc_bs) +
-                       cell * (which ? a.vsc_cs : a.ksc_cs) + ((long long)g * NB + blk) * 2;
-            *(uint16_t*)sc = sb;
-        } else {
-            // index keys: 4 elements of (b, t)
+                            cell * (which ? a.vq_cs : a.kq_cs) + (long long)g * a.D + 32 * blk +
+                            4 * sub;
+            *(uint32_t*)codes = word;
+            if (sub == 0) {
+                char* sc = (char*)(which ? a.Vsc : a.Ksc) +
+                           (long long)b * (which ? a.vsc_bs : a.ksc_bs) +
+                           cell * (which ? a.vsc_cs : a.ksc_cs) + ((long long)g * NB + blk) * 2;
+                *(uint16_t*)sc = sb;
+            }
+        } else if (w < total) {
+            // index keys: 4 elements of (b, t) (n_quant is a multiple of 256,
+            // so this whole workgroup is in the index range)
             const long long r = w - n_quant;
             const int per = a.DI / 4;
             const int i = (int)(r % per);
@@ -135,11 +142,14 @@ __global__ __launch_bounds__(256) void k_kv_append(AppendLaunch a, long long n_q
 
 hipError_t launch_kv_append(const AppendLaunch& a, hipStream_t s)
 {
-    const long long n_quant = (long long)a.B * a.T * a.Hkv * (a.D / 32) * 2;
+    // Quantisation lanes rounded up to whole workgroups, so no workgroup
+    // mixes the two kinds of items (the extra lanes are idle).
+    const long long q_lanes = (long long)a.B * a.T * a.Hkv * (a.D / 32) * 2 * 8;
+    const long long n_quant = (q_lanes + 255) / 256 * 256;
     const long long n_idx = a.kidx_new ? (long long)a.B * a.T * (a.DI / 4) : 0;
-    const long long total = n_quant + n_idx;
-    const long long blocks = (total + 255) / 256;
-    k_kv_append<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(a, n_quant, n_idx);
+    const long long blocks = (n_quant + n_idx + 255) / 256;
+    k_kv_append<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(a, q_lanes, n_quant,
+                                                                          n_idx);
     return hipGetLastError();
 }
 
