@@ -79,6 +79,8 @@ class Oracle:
         lib.qo_attend.restype = _I
         lib.qo_merge.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P]
         lib.qo_merge.restype = _I
+        lib.qo_merge_gated.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
+        lib.qo_merge_gated.restype = _I
         lib.qo_quant_row.argtypes = [_I, _P, _P, _P]
         lib.qo_quant_row.restype = _I
         lib.qo_kv_append.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
@@ -171,6 +173,26 @@ class Oracle:
                                    _ptr(np.ascontiguousarray(po[b])), _ptr(ob))
             if rc != 0:
                 raise ValueError("oracle qo_merge rejected its arguments")
+            out[b] = ob
+        return out
+
+    def merge_gated(self, pm, pl, po, gate) -> np.ndarray:
+        """Merge, then the elementwise sigmoid output gate (gate [B][T][Hq][D],
+        fp32 or fp16)."""
+        pm = np.ascontiguousarray(pm, dtype=np.float64)
+        pl = np.ascontiguousarray(pl, dtype=np.float64)
+        po = np.ascontiguousarray(po, dtype=np.float64)
+        gate = np.ascontiguousarray(np.asarray(gate).astype(np.float64))
+        B, T, Hq, P, D = po.shape
+        out = np.empty((B, T, Hq, D), dtype=np.float64)
+        for b in range(B):
+            ob = np.empty((T, Hq, D))
+            rc = self.lib.qo_merge_gated(T, Hq, P, D, _ptr(np.ascontiguousarray(pm[b])),
+                                         _ptr(np.ascontiguousarray(pl[b])),
+                                         _ptr(np.ascontiguousarray(po[b])),
+                                         _ptr(np.ascontiguousarray(gate[b])), _ptr(ob))
+            if rc != 0:
+                raise ValueError("oracle qo_merge_gated rejected its arguments")
             out[b] = ob
         return out
 

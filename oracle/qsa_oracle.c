@@ -428,3 +428,25 @@ int qo_kv_append(int T, int N, int Hkv, int D, int di, int pos0, const float* k_
     }
     return 0;
 }
+
+/* ------------------------------------------------------- gated output --- */
+
+/*
+ * Output gate ([r20] section 3 pairs the attention with a gate: random
+ * "q/gate" inputs, "attention + gate" checked together; [r5c] Target 2
+ * sizes q and gate together at 12288 floats per token, i.e. one gate value
+ * per output element of the 24 x 256 heads).  The gate function is not
+ * stated; the plain reading is an elementwise logistic sigmoid:
+ *   out[t][h][d] = merge(...)[t][h][d] * 1 / (1 + exp(-gate[t][h][d])).
+ *   gate [T][Hq][D] in double (from fp32 or fp16 inputs)
+ */
+int qo_merge_gated(int T, int Hq, int P, int D, const double* pm, const double* pl,
+                   const double* po, const double* gate, double* out)
+{
+    const int rc = qo_merge(T, Hq, P, D, pm, pl, po, out);
+    if (rc != 0)
+        return rc;
+    for (size_t i = 0; i < (size_t)T * Hq * D; ++i)
+        out[i] *= 1.0 / (1.0 + exp(-gate[i]));
+    return 0;
+}

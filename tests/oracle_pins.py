@@ -476,6 +476,32 @@ def pin_append_placement(orc):
                     assert np.array_equal(scales[b, pos0 + t, g], rs)
 
 
+def pin_gate(orc):
+    """The gated merge is the plain merge times scipy's logistic sigmoid of
+    the gate, elementwise; gate 0 halves the output exactly, large gates
+    pass it through or shut it."""
+    from scipy.special import expit
+    rng = np.random.default_rng(83)
+    B, T, Hq, P, D = 2, 3, 4, 5, 32
+    pm = rng.normal(size=(B, T, Hq, P)) * 3
+    pm[0, 1, 2, :2] = -np.inf                                   # empty chunks
+    pl = rng.uniform(0.5, 4, size=(B, T, Hq, P))
+    pl[np.isneginf(pm)] = 0
+    po = rng.normal(size=(B, T, Hq, P, D))
+    po[np.isneginf(pm)] = 0
+    gate = rng.normal(size=(B, T, Hq, D)) * 4
+    gate[0, 0, 0, :3] = (0.0, 60.0, -60.0)
+    plain = orc.merge(pm, pl, po)
+    got = orc.merge_gated(pm, pl, po, gate)
+    assert np.allclose(got, plain * expit(gate), rtol=1e-13, atol=0)
+    assert got[0, 0, 0, 0] == plain[0, 0, 0, 0] * 0.5
+    assert abs(got[0, 0, 0, 1] - plain[0, 0, 0, 1]) <= 1e-25 * abs(plain[0, 0, 0, 1]) + 1e-300
+    assert abs(got[0, 0, 0, 2]) <= 1e-25 * abs(plain[0, 0, 0, 2])
+    g16 = gate.astype(np.float16)
+    assert np.allclose(orc.merge_gated(pm, pl, po, g16),
+                       plain * expit(g16.astype(np.float64)), rtol=1e-13, atol=0)
+
+
 ALL_PINS = [
     pin_half_decode_exhaustive,
     pin_half_encode,
@@ -492,4 +518,5 @@ ALL_PINS = [
     pin_quantiser_exact,
     pin_quantiser_ties,
     pin_append_placement,
+    pin_gate,
 ]

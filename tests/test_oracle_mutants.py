@@ -87,6 +87,12 @@ MUTANTS = [
     ("append_wrong_cell",
      "const size_t cell = (size_t)(pos0 + t);",
      "const size_t cell = (size_t)(pos0 + t + 1 < N ? pos0 + t + 1 : pos0 + t);"),
+    ("gate_sign",
+     "out[i] *= 1.0 / (1.0 + exp(-gate[i]));",
+     "out[i] *= 1.0 / (1.0 + exp(gate[i]));"),
+    ("gate_tanh",
+     "out[i] *= 1.0 / (1.0 + exp(-gate[i]));",
+     "out[i] *= 0.5 * (1.0 + tanh(gate[i]));"),
     ("max_not_subtracted_last_chunk_only",
      "for (int c = 0; c < P; ++c)\n            if (m[c] > M)",
      "for (int c = 0; c + 1 < P; ++c)\n            if (m[c] > M)"),
