@@ -1,9 +1,10 @@
 """Throughput benchmark of the QSA hot path on one MI355X.
 
-One step = qsa_kv_append -> qsa_index_topk -> qsa_attend -> qsa_merge over
-a batch of B independent problems (seeded synthetic caches already resident
-in HBM): the step's T new tokens are quantised into their cells of the
-cache, then selected from and attended to.
+One step = qsa_kv_append -> qsa_index_topk -> qsa_attend -> qsa_merge_gated
+over a batch of B independent problems (seeded synthetic caches already
+resident in HBM): the step's T new tokens are quantised into their cells of
+the cache, then selected from and attended to, and the merged output is
+gated.
 The default workload is the decode step (1 token, 24 x 256 query heads,
 2 KV heads, 8192 cached cells, index dim 128, top-2048) over B = 256
 independent caches, so the working set (~2.7 GB) is far larger than the
@@ -62,7 +63,7 @@ def algorithmic_bytes(p: dict, B: int, n_sel_total: int) -> dict:
     index = B * (nvis_max * di * 2 + T * di * 2) if selects else 0
     per_cell = Hkv * (D + (D // 32) * 2) * 2          # K and V codes + scales
     attend = n_sel_total * (per_cell + 4) + B * T * Hq * D * qbytes
-    out = B * T * Hq * D * obytes
+    out = B * T * Hq * D * (obytes + qbytes)              # output and its gate
     return dict(append=append, index=index, attend=attend, out=out,
                 total=append + index + attend + out)
 
@@ -184,6 +185,8 @@ def main() -> None:
     i_new = torch.randn((B, T_new, inp["di"]), generator=gen, device="cuda")
     adesc = qsa.append_desc(batch=B, T=T_new, n_cells=inp["N"], pos0=inp["pos0"],
                             Hkv=inp["Hkv"], D=inp["D"], d_idx=inp["di"])
+    gate = torch.randn(tuple(dev["q"].shape), generator=gen, device="cuda").to(dev["q"].dtype)
+    dev["gate"] = gate
 
     def append():
         qsa.qsa_kv_append(adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"], dev["Vq"],
@@ -215,7 +218,7 @@ def main() -> None:
         e[2].record(stream)
         path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"])
         e[3].record(stream)
-        path.merge()
+        path.merge(gate=gate)
         e[4].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -233,7 +236,7 @@ def main() -> None:
     gbs = by["total"] / (step_ms * 1e-3) / 1e9
 
     # Dominant kernel: the stage with the largest average time.
-    names = ["kv_append", "index_topk", "attend", "merge"]
+    names = ["kv_append", "index_topk", "attend", "merge_gated"]
     dom = int(np.argmax(stage_ms))
     att_ms = stage_ms[2]
     if names[dom] == "attend" and args.algo == "vector":
@@ -254,7 +257,8 @@ def main() -> None:
                     algorithmic_bytes=by["attend"],
                     definition_tflops=round(flops / (att_ms * 1e-3) / 1e12, 2))
     else:
-        sb = {"index_topk": by["index"], "merge": by["out"], "kv_append": by["append"]}[names[dom]]
+        sb = {"index_topk": by["index"], "merge_gated": by["out"],
+              "kv_append": by["append"]}[names[dom]]
         achieved = sb / (stage_ms[dom] * 1e-3) / 1e9
         roof = dict(kernel=names[dom], bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),

@@ -210,6 +210,21 @@ QSA_API int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* ou
               void* stream);
 
 /* ------------------------------------------------------------------------
+ * qsa_merge_gated -- qsa_merge followed by the output gate the "opus r20
+ * ..." page pairs the attention with (section 3: random "q/gate" inputs,
+ * "attention + gate" checked together; the "Round 5 Track C ..." page,
+ * Target 2, sizes q and gate together at 12288 floats per token: one gate
+ * value per output element).  The gate function is not stated; the plain
+ * reading is an elementwise logistic sigmoid:
+ *   out[b][t][h][d] = merged[b][t][h][d] * 1 / (1 + exp(-gate[b][t][h][d]))
+ * computed in fp32 before the optional fp16 rounding of out.
+ * gate: [B][T][Hq][D] in the query dtype (desc->q_dtype), 16-byte aligned;
+ * NULL gives qsa_merge.  Other arguments, errors and support as qsa_merge.
+ * --------------------------------------------------------------------- */
+QSA_API int qsa_merge_gated(const qsa_attn_desc* desc, const float* partials, const void* gate,
+                            void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * qsa_kv_append -- write T new tokens into the cache, the step that feeds
  * the path: their K and V rows become int8 codes with one fp16 scale per
  * 32 elements (the cache format of the "opus r20 ..." page, section 3:

@@ -31,8 +31,9 @@ ALGOS = {"matrix": qsa.QSA_ATTEND_MATRIX, "vector": qsa.QSA_ATTEND_VECTOR}
 
 
 def run_gpu(inp: dict, *, P: int | None = None, strides=None, dev=None, ids=None,
-            n_sel=None, index=True, algo: str = "matrix") -> dict:
-    """Runs index_topk -> attend -> merge on cuda:0 and returns numpy copies."""
+            n_sel=None, index=True, algo: str = "matrix", gate=None) -> dict:
+    """Runs index_topk -> attend -> merge (gated when a gate array is given)
+    on cuda:0 and returns numpy copies."""
     path = qsa.path_for(inp, P=P, strides=strides, algo=ALGOS[algo])
     dev = qsa.to_device(inp) if dev is None else dev
     if index:
@@ -41,7 +42,7 @@ def run_gpu(inp: dict, *, P: int | None = None, strides=None, dev=None, ids=None
     nsel_t = path.n_sel if n_sel is None else torch.from_numpy(n_sel).cuda()
     path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"], ids=ids_t,
                 n_sel=nsel_t)
-    path.merge()
+    path.merge(gate=None if gate is None else torch.from_numpy(np.ascontiguousarray(gate)).cuda())
     torch.cuda.synchronize()
     return dict(ids=path.ids.cpu().numpy(), n_sel=path.n_sel.cpu().numpy(),
                 pm=path.pm.cpu().numpy(), pl=path.pl.cpu().numpy(),

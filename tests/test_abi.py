@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("qsa_index_topk", "qsa_attend", "qsa_merge", "qsa_index_topk_workspace",
-              "qsa_partials_floats", "qsa_status_string", "qsa_version", "qsa_kv_append"):
+              "qsa_partials_floats", "qsa_status_string", "qsa_version", "qsa_kv_append",
+              "qsa_merge_gated"):
         assert n in names
 
 
@@ -148,6 +149,15 @@ def test_attn_pointer_checks_and_sizes():
     d2 = _adesc(strides=dict(kq_cell_stride=1088, ksc_cell_stride=1088,
                              vq_cell_stride=1088, vsc_cell_stride=1088))
     assert L.qsa_partials_floats(ctypes.byref(d2)) > 0
+
+
+def test_merge_gated_checks():
+    L = qb.lib()
+    d = _adesc()
+    assert L.qsa_merge_gated(ctypes.byref(d), 16, 8, 16, None) == INVALID   # misaligned gate
+    assert L.qsa_merge_gated(ctypes.byref(d), None, 16, 16, None) == INVALID
+    assert L.qsa_merge_gated(None, 16, 16, 16, None) == INVALID
+    assert L.qsa_merge_gated(ctypes.byref(_adesc(P=65)), 16, 16, 16, None) == UNSUPPORTED
 
 
 def test_null_descriptor():

@@ -261,3 +261,23 @@ def test_fp32_level_precision(orc, cfg, batch, algo):
     assert rel <= 1e-5, rel
     fin = np.isfinite(ref["pm"])
     assert np.abs(res["pm"].astype(np.float64)[fin] - ref["pm"][fin]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("cfg,batch", [("decode", 2), ("tiny", 3), ("prompt_small", 1)])
+def test_gated_merge(orc, cfg, batch):
+    """qsa_merge_gated: the merged output times sigmoid(gate) elementwise,
+    with an fp32 gate (fp32 q) or an fp16 gate (fp16 q, fp16 output)."""
+    if cfg == "prompt_small":
+        cfg = dict(T=64, N=4096, di=128, k=256, dense_max=259, Hq=24, Hkv=2, D=256, P=1,
+                   q_dtype="f16", out_dtype="f16", heavy_tail=False)
+    inp = make_inputs(cfg, seed=95, batch=batch)
+    rng = np.random.default_rng(96)
+    gdt = np.float16 if inp["q"].dtype == np.float16 else np.float32
+    gate = (rng.normal(size=inp["q"].shape) * 3).astype(gdt)
+    gate.reshape(-1)[:4] = (0.0, 40.0, -40.0, -5.0)
+    say(f"[gate] {inp['T']} tokens, gate {gdt.__name__}")
+    res = run_gpu(inp, gate=gate)
+    ref = _oracle_all(orc, inp, inp["P"])
+    want = orc.merge_gated(ref["pm"], ref["pl"], ref["po"], gate)
+    assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+    assert_out_close(res["out"], want, "gated out")

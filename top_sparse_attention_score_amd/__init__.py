@@ -7,5 +7,5 @@ include/qsa.h); ``qsa`` is the ctypes binding.
 from .qsa import (QSA_ATTEND_AUTO, QSA_ATTEND_MATRIX, QSA_ATTEND_VECTOR,  # noqa: F401
                   QSA_F16, QSA_F32, AppendDesc, AttnDesc, IndexDesc, QsaError,  # noqa: F401
                   QsaPath, append_desc, attn_desc, index_desc, path_for, qsa_attend,
-                  qsa_index_topk, qsa_kv_append,
+                  qsa_index_topk, qsa_kv_append, qsa_merge_gated,
                   qsa_index_topk_workspace, qsa_merge, qsa_partials_floats, to_device)

@@ -86,6 +86,7 @@ int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
     L->q_f16 = d->q_dtype == QSA_F16;
     L->out_f16 = d->out_dtype == QSA_F16;
     L->algo = d->algo;
+    L->gate = nullptr;
     return QSA_OK;
 }
 
@@ -190,22 +191,30 @@ int qsa_attend(const qsa_attn_desc* desc, const void* q, const int8_t* Kq, const
     return QSA_OK;
 }
 
-int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* out, void* stream)
+int qsa_merge_gated(const qsa_attn_desc* desc, const float* partials, const void* gate,
+                    void* out, void* stream)
 {
     qsa::AttnLaunch a;
     const int st = check_attn(desc, &a);
     if (st != QSA_OK)
         return st;
-    if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16))
+    if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16) ||
+        (gate && !aligned(gate, 16)))
         return QSA_ERR_INVALID_ARG;
     const size_t rows = partial_rows(desc);
     a.pm = (float*)partials;
     a.pl = (float*)partials + rows;
     a.po = (float*)partials + 2 * rows;
     a.out = out;
+    a.gate = gate;
     if (qsa::launch_merge(a, (hipStream_t)stream) != hipSuccess)
         return QSA_ERR_HIP;
     return QSA_OK;
+}
+
+int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* out, void* stream)
+{
+    return qsa_merge_gated(desc, partials, nullptr, out, stream);
 }
 
 int qsa_kv_append(const qsa_append_desc* d, const float* k_new, const float* v_new,

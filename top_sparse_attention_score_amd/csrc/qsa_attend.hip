@@ -346,13 +346,16 @@ constexpr int kMergeWaves = 4;
 // many chunks over more waves).  Per element: M = max_c m_c, then over the
 // chunks in order e = exp(m_c - M) (0 for an empty chunk), L = fma(l_c, e,
 // L), y = fma(o_c, e, y), and one division.  An empty chunk has l = o = 0,
-// so its zero weight leaves L and y bitwise unchanged.
+// so its zero weight leaves L and y bitwise unchanged.  With a gate (same
+// layout and dtype as q), the result is multiplied by 1 / (1 + exp(-g)).
 template <int D, int EPL, bool OUTF16>
 __global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restrict__ pm,
                                                             const float* __restrict__ pl,
                                                             const float* __restrict__ po,
                                                             void* __restrict__ out, int P,
-                                                            long long rows)
+                                                            long long rows,
+                                                            const void* __restrict__ gate,
+                                                            int gate_f16)
 {
     constexpr int LPR = D / EPL;   // lanes per row
     constexpr int RPW = 64 / LPR;  // rows per wave (D = 64, EPL = 1: one row per wave)
@@ -402,6 +405,35 @@ __global__ __launch_bounds__(64 * kMergeWaves) void k_merge(const float* __restr
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
         res[e] = (L > 0.f) ? y[e] / L : 0.f;
+    if (gate) {
+        // output gate: res * sigmoid(g), elementwise
+        float gv[EPL];
+        if (gate_f16) {
+            const _Float16* gp = (const _Float16*)gate + r * D + de;
+            if constexpr (EPL == 4) {
+                const half4_t g4 = *(const half4_t*)gp;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gv[e] = (float)g4[e];
+            } else {
+                gv[0] = (float)gp[0];
+            }
+        } else {
+            const float* gp = (const float*)gate + r * D + de;
+            if constexpr (EPL == 4) {
+                const float4 g4 = *(const float4*)gp;
+                gv[0] = g4.x;
+                gv[1] = g4.y;
+                gv[2] = g4.z;
+                gv[3] = g4.w;
+            } else {
+                gv[0] = gp[0];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            res[e] *= 1.f / (1.f + expf(-gv[e]));
+    }
     if constexpr (OUTF16) {
         _Float16* dst = (_Float16*)out + r * D + de;
         if constexpr (EPL == 4)
@@ -474,10 +506,13 @@ static void launch_merge_de(const AttnLaunch& a, long long rows, hipStream_t s)
 {
     const long long lanes = rows * (D / EPL);
     const unsigned grid = (unsigned)((lanes + 64 * kMergeWaves - 1) / (64 * kMergeWaves));
+    const int gate_f16 = a.q_f16 ? 1 : 0;
     if (a.out_f16)
-        k_merge<D, EPL, true><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+        k_merge<D, EPL, true><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows,
+                                                               a.gate, gate_f16);
     else
-        k_merge<D, EPL, false><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P, rows);
+        k_merge<D, EPL, false><<<grid, 64 * kMergeWaves, 0, s>>>(a.pm, a.pl, a.po, a.out, a.P,
+                                                                rows, a.gate, gate_f16);
 }
 
 hipError_t launch_merge(const AttnLaunch& a, hipStream_t s)

@@ -44,6 +44,7 @@ struct AttnLaunch {
     float* pl;
     float* po;
     void* out;
+    const void* gate;  // output gate (q layout and dtype) or null
 };
 
 // True if a kernel variant exists for (G, D, q dtype).

@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_attend.restype = _c_int
         L.qsa_merge.argtypes = [ctypes.POINTER(AttnDesc), _vp, _vp, _vp]
         L.qsa_merge.restype = _c_int
+        L.qsa_merge_gated.argtypes = [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp]
+        L.qsa_merge_gated.restype = _c_int
         L.qsa_kv_append.argtypes = [ctypes.POINTER(AppendDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp]
         L.qsa_kv_append.restype = _c_int
@@ -166,6 +168,11 @@ def qsa_merge(desc: AttnDesc, partials, out, stream=None) -> None:
            "qsa_merge")
 
 
+def qsa_merge_gated(desc: AttnDesc, partials, gate, out, stream=None) -> None:
+    _check(lib().qsa_merge_gated(ctypes.byref(desc), _ptr(partials), _ptr(gate), _ptr(out),
+                                 _stream(stream)), "qsa_merge_gated")
+
+
 def qsa_kv_append(desc: AppendDesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
                   stream=None) -> None:
     _check(lib().qsa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(kidx_new),
@@ -215,13 +222,16 @@ class QsaPath:
         qsa_attend(self.adesc, q, Kq, Ksc, Vq, Vsc, self.ids if ids is None else ids,
                    self.n_sel if n_sel is None else n_sel, self.partials, stream)
 
-    def merge(self, stream=None):
-        qsa_merge(self.adesc, self.partials, self.out, stream)
+    def merge(self, stream=None, gate=None):
+        if gate is None:
+            qsa_merge(self.adesc, self.partials, self.out, stream)
+        else:
+            qsa_merge_gated(self.adesc, self.partials, gate, self.out, stream)
 
     def run(self, dev: dict, stream=None):
         self.index(dev["q_idx"], dev["K_idx"], stream)
         self.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"], stream)
-        self.merge(stream)
+        self.merge(stream, gate=dev.get("gate"))
         return self.out
 
 
