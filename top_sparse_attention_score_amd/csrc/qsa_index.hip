@@ -19,8 +19,7 @@
 //   k_scan_select one token with a row of at most 16384 cells (decode):
 //                scan and select fused in one workgroup per token.
 //   k_idx_gemm   prompt chunk (T > 16): [T x d_idx] x [d_idx x N] on MFMA
-//                (v_mfma_f32_16x16x16_f16), 64 tokens x 64 cells per
-//                workgroup.
+//                (v_mfma_f32_16x16x32_f16), 64 tokens x 256 cells per wave.
 //   k_sel_row    exact top-k of rows up to 65536 cells, one workgroup per
 //                token, keys in registers.
 //   k_sel_*      exact top-k over the score keys of longer rows, tiled over
@@ -170,69 +169,81 @@ __global__ __launch_bounds__(256) void k_idx_mscan(const _Float16* __restrict__ 
 
 // ---------------------------------------------------------------- gemm ---
 
-// Each wave computes 32 tokens x 32 cells as 2 x 2 MFMA 16x16 blocks.  In an
-// MFMA step lane group g (lanes 16g..16g+15) supplies k-slots 4g..4g+3; here
-// lane group g instead supplies row elements [g*DI/4 + 4s, g*DI/4 + 4s + 4) at
-// step s for both operands, so over the DI/16 steps every element of the dot
-// product is used exactly once (a permutation of the reduction index).
+// A wave keeps the index queries of 64 tokens in registers (A operands of
+// v_mfma_f32_16x16x32_f16, four 16-token row blocks) and walks 8 blocks of
+// 32 consecutive cells, so every key row is read once per 64 tokens and
+// every query once per 256 cells.  The reduction index is permuted as in
+// k_idx_mscan (lane group g supplies elements 64*(s/2) + 16*g + 8*(s%2) ..
+// +7 at step s, in both operands), so a lane reads 32 contiguous bytes per
+// step pair.  Result of a 16x16 block: lane l, element e holds token row
+// 4*(l/16)+e and cell column l%16.  Scores are exact on the seeded grid in
+// any accumulation order.
+constexpr int kGemmTok = 64;    // tokens per wave
+constexpr int kGemmBlocks = 8;  // 32-cell blocks per wave
 template <int DI>
 __global__ __launch_bounds__(256) void k_idx_gemm(const _Float16* __restrict__ q_idx,
                                                   const _Float16* __restrict__ K_idx,
                                                   uint32_t* __restrict__ keys, int T, int N,
                                                   int nvis_max)
 {
-    constexpr int KQ = DI / 4;
-    constexpr int STEPS = DI / 16;
+    typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+    constexpr int KS = DI / 32;  // MFMA steps per row
     const int b = blockIdx.z;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int tok0 = blockIdx.y * 64 + (w >> 1) * 32;
-    const int cell0 = blockIdx.x * 64 + (w & 1) * 32;
     const int r = lane & 15, grp = lane >> 4;
+    const int tok0 = blockIdx.y * kGemmTok;
+    const int cell_base = (blockIdx.x * 4 + w) * (32 * kGemmBlocks);
+    if (cell_base >= nvis_max)
+        return;
 
-    half4_t a[2][STEPS], kb[2][STEPS];
+    auto kofs = [&](int st) { return 64 * (st >> 1) + 16 * grp + 8 * (st & 1); };
+    h8_t qa[4][KS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int tok = min(tok0 + 16 * i + r, T - 1);
-        const half4_t* src = (const half4_t*)(q_idx + ((size_t)b * T + tok) * DI + grp * KQ);
+        const _Float16* src = q_idx + ((size_t)b * T + tok) * DI;
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s)
-            a[i][s] = src[s];
+        for (int st = 0; st < KS; ++st)
+            qa[i][st] = *(const h8_t*)(src + kofs(st));
     }
+#pragma unroll 1
+    for (int cb = 0; cb < kGemmBlocks; ++cb) {
+        const int c0 = cell_base + 32 * cb;
+        if (c0 >= nvis_max)
+            break;
+        h8_t kb[2][KS];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int cell = min(cell0 + 16 * jj + r, nvis_max - 1);
-        const half4_t* src = (const half4_t*)(K_idx + ((size_t)b * N + cell) * DI + grp * KQ);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int cell = min(c0 + 16 * jj + r, nvis_max - 1);
+            const _Float16* src = K_idx + ((size_t)b * N + cell) * DI;
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s)
-            kb[jj][s] = src[s];
-    }
-    float4_t acc[2][2];
+            for (int st = 0; st < KS; ++st)
+                kb[jj][st] = *(const h8_t*)(src + kofs(st));
+        }
+        float4_t acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-            acc[i][jj] = float4_t{0.f, 0.f, 0.f, 0.f};
+            for (int jj = 0; jj < 2; ++jj) {
+                acc[i][jj] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[i][s], kb[jj][s],
-                                                                   acc[i][jj], 0, 0, 0);
-    // Result layout of a 16x16 block: lane l, element e holds row 4*(l/16)+e,
-    // column l%16 (rows = tokens, columns = cells).
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tok = tok0 + 16 * i + 4 * grp + e;
-                const int cell = cell0 + 16 * jj + r;
-                if (tok < T && cell < nvis_max)
-                    keys[((size_t)b * T + tok) * N + cell] = score_key(acc[i][jj][e]);
+                for (int st = 0; st < KS; ++st)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i][st], kb[jj][st],
+                                                                        acc[i][jj], 0, 0, 0);
             }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int cell = c0 + 16 * jj + r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = tok0 + 16 * i + 4 * grp + e;
+                    if (tok < T && cell < nvis_max)
+                        keys[((size_t)b * T + tok) * N + cell] = score_key(acc[i][jj][e]);
+                }
+            }
+    }
 }
 
 // -------------------------------------------------------------- select ---
@@ -963,7 +974,9 @@ static void launch_scan(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipS
 template <int DI>
 static void launch_gemm(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipStream_t s)
 {
-    dim3 grid((nvis_max + 63) / 64, (a.T + 63) / 64, a.B);
+    constexpr int cells_per_block = 4 * 32 * kGemmBlocks;
+    dim3 grid((nvis_max + cells_per_block - 1) / cells_per_block,
+              (a.T + kGemmTok - 1) / kGemmTok, a.B);
     k_idx_gemm<DI><<<grid, 256, 0, s>>>((const _Float16*)a.q_idx, (const _Float16*)a.K_idx,
                                          keys, a.T, a.N, nvis_max);
 }
