@@ -22,9 +22,7 @@
 
 namespace qsa {
 
-namespace {
-
-__device__ __forceinline__ uint16_t f16_bits(_Float16 h)
+static __device__ __forceinline__ uint16_t f16_bits(_Float16 h)
 {
     uint16_t u;
     __builtin_memcpy(&u, &h, 2);
@@ -32,14 +30,14 @@ __device__ __forceinline__ uint16_t f16_bits(_Float16 h)
 }
 
 // Value of a non-negative binary16 pattern (0x7c00 and up: infinity).
-__device__ __forceinline__ float f16_value(uint16_t u)
+static __device__ __forceinline__ float f16_value(uint16_t u)
 {
     return u >= 0x7c00u ? INFINITY : half_bits_to_float(u);
 }
 
 // fp16 pattern nearest to a / 127 for finite a >= 0, ties to the even
 // pattern, never infinity (saturates at 65504).
-__device__ __forceinline__ uint16_t scale_bits(float a)
+static __device__ __forceinline__ uint16_t scale_bits(float a)
 {
     const uint16_t h = f16_bits((_Float16)(a / 127.0f));
     uint16_t best = h;
@@ -137,8 +135,6 @@ __global__ __launch_bounds__(256) void k_kv_append(AppendLaunch a, long long q_l
         }
     }
 }
-
-}  // namespace
 
 hipError_t launch_kv_append(const AppendLaunch& a, hipStream_t s)
 {
