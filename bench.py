@@ -33,6 +33,11 @@ HBM_PEAK_GBS = 8000.0
 # x 2 flop x 2.4 GHz.
 FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12   # 78.6
 
+# Split count of the single-problem latency run where the workload leaves it
+# free (decode: one problem has only Hkv * P waves of attention, so more
+# chunks); the others keep the split their definition fixes.
+LATENCY_P = {"decode": 32}
+
 WORKLOADS = {
     # name: (datagen config, default batch, description)
     "decode": ("decode", 256, "decode step: 1 token, 24x256 q heads, 2 KV heads, 8192 cells, "
@@ -132,6 +137,58 @@ def cpu_baseline(inp_cfg: str, target_s: float, P: int) -> dict:
                        f"{t_used:.1f} s single-threaded")
 
 
+def single_problem_latency(qsa, base: dict, P: int, algo_code: int, steps: int = 50) -> dict:
+    """One problem (B = 1) per step, the latency-bound case: the same step
+    (append -> index_topk -> attend -> gated merge) launched eagerly, and
+    captured once in a HIP graph and replayed; microseconds per step."""
+    import torch
+    inp = {k: (v[:1] if hasattr(v, "shape") and getattr(v, "ndim", 0) and k in
+               ("q_idx", "K_idx", "q", "Kq", "Ksc", "Vq", "Vsc") else v)
+           for k, v in base.items()}
+    inp["batch"] = 1
+    dev = qsa.to_device(inp)
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    T, Hkv, D, di = inp["T"], inp["Hkv"], inp["D"], inp["di"]
+    k_new = torch.randn((1, T, Hkv, D), generator=gen, device="cuda")
+    v_new = torch.randn((1, T, Hkv, D), generator=gen, device="cuda")
+    i_new = torch.randn((1, T, di), generator=gen, device="cuda")
+    dev["gate"] = torch.randn(tuple(dev["q"].shape), generator=gen,
+                              device="cuda").to(dev["q"].dtype)
+    adesc = qsa.append_desc(batch=1, T=T, n_cells=inp["N"], pos0=inp["pos0"], Hkv=Hkv, D=D,
+                            d_idx=di)
+    path = qsa.path_for(inp, P=P, algo=algo_code)
+    side = torch.cuda.Stream()
+
+    def step(stream=None):
+        qsa.qsa_kv_append(adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"], dev["Vq"],
+                          dev["Vsc"], dev["K_idx"], stream=stream)
+        path.run(dev, stream=stream)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / steps * 1e3, 2)
+
+    eager = timed(step)
+    g = torch.cuda.CUDAGraph()
+    step()
+    torch.cuda.synchronize()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return dict(eager=eager, graph=timed(g.replay))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +201,8 @@ def main() -> None:
                     help="distinct seeded problems, tiled to the batch on the GPU")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-latency", action="store_true",
+                    help="skip the single-problem (B = 1) latency measurement")
     ap.add_argument("--algo", default="matrix", choices=["matrix", "vector"],
                     help="qsa_attend kernel family")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -279,6 +338,9 @@ def main() -> None:
     }
     if inp["q_dtype"] == "f16":
         line["dtype"] = "f16 in, f32 accumulate"
+    if not args.no_latency:
+        p_lat = LATENCY_P.get(args.workload, P)
+        line["latency_b1_us"] = dict(P=p_lat, **single_problem_latency(qsa, base, p_lat, algo_code))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg_name, args.cpu_seconds, P)

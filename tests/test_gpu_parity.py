@@ -281,3 +281,49 @@ def test_gated_merge(orc, cfg, batch):
     want = orc.merge_gated(ref["pm"], ref["pl"], ref["po"], gate)
     assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
     assert_out_close(res["out"], want, "gated out")
+
+
+def test_graph_replay_matches_eager(orc):
+    """The whole step (append -> index_topk -> attend -> gated merge) captured
+    in a HIP graph: every replay, with eager work and synchronisations in
+    between, gives bitwise the eager result (the path records no memset)."""
+    import top_sparse_attention_score_amd as qsa
+    inp = make_inputs("decode", seed=97, batch=1)
+    dev = qsa.to_device(inp)
+    rng = np.random.default_rng(98)
+    B, T, Hkv, D, di = 1, inp["T"], inp["Hkv"], inp["D"], inp["di"]
+    k_new = torch.from_numpy(rng.normal(size=(B, T, Hkv, D)).astype(np.float32)).cuda()
+    v_new = torch.from_numpy(rng.normal(size=(B, T, Hkv, D)).astype(np.float32)).cuda()
+    i_new = torch.from_numpy(rng.normal(size=(B, T, di)).astype(np.float32)).cuda()
+    dev["gate"] = torch.from_numpy(rng.normal(size=inp["q"].shape).astype(np.float32)).cuda()
+    adesc = qsa.append_desc(batch=B, T=T, n_cells=inp["N"], pos0=inp["pos0"], Hkv=Hkv, D=D,
+                            d_idx=di)
+    path = qsa.path_for(inp)
+    side = torch.cuda.Stream()
+
+    def step(stream):
+        qsa.qsa_kv_append(adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"], dev["Vq"],
+                          dev["Vsc"], dev["K_idx"], stream=stream)
+        path.run(dev, stream=stream)
+
+    step(None)
+    torch.cuda.synchronize()
+    eager = path.out.clone()
+    ids = path.ids.clone()
+    g = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        path.out.zero_()
+        path.ids.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(path.out, eager), rep
+        assert torch.equal(path.ids, ids), rep
+        step(None)                      # eager work between replays
+        torch.cuda.synchronize()

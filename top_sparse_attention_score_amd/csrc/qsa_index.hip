@@ -989,7 +989,9 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
     // Scores are needed only when some token keeps fewer cells than it sees.
     const int nvis_max = a.pos0 + a.T;  // cells visible to the last token
     const bool any_select = token_selects(nvis_max, a.k, a.dense_max);
-    if (any_select && a.T == 1 && a.N <= kRowThreads * 16) {
+    // The fused kernel runs one workgroup per token; with fewer tokens than
+    // about half the CUs the chip-wide scan is faster.
+    if (any_select && a.T == 1 && a.N <= kRowThreads * 16 && a.B >= 128) {
         const uint4* q = (const uint4*)a.q_idx;
         const uint4* K = (const uint4*)a.K_idx;
 #define QSA_FUSED(DI, KPT)                                                               \
