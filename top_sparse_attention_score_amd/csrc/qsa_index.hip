@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void k_idx_scan(const uint4* __restrict__ q_id
 // lane reads 32 contiguous bytes and the four groups a whole 128-byte line
 // of its cell.  Every lane then holds four tokens' scores of one cell, with
 // no cross-lane reduction; on the seeded grid inputs fp32 accumulation is
-// exact in any order.  Four groups (64 cells) are in flight per wave.
+// exact in any order.
+constexpr int kMscanGroups = 2;  // 16-cell groups in flight per wave (measured: 2 beats 4 and 8)
 template <int DI>
 __global__ __launch_bounds__(256) void k_idx_mscan(const _Float16* __restrict__ q_idx,
                                                    const _Float16* __restrict__ K_idx,
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) void k_idx_mscan(const _Float16* __restrict__ 
 {
     typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
     constexpr int KS = DI / 32;   // MFMA steps per key row
-    constexpr int U = 4;          // 16-cell groups per wave and pass
+    constexpr int U = kMscanGroups;  // 16-cell groups per wave
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, q4 = lane >> 4;
@@ -1013,7 +1014,7 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
             else
                 launch_scan<128>(a, w.keys, nvis_max, s);
         } else if (a.T <= 16) {
-            const dim3 grid((nvis_max + 255) / 256, a.B);  // 4 waves x 64 cells
+            const dim3 grid((nvis_max + 64 * kMscanGroups - 1) / (64 * kMscanGroups), a.B);
             if (a.DI == 64)
                 k_idx_mscan<64><<<grid, 256, 0, s>>>((const _Float16*)a.q_idx,
                                                      (const _Float16*)a.K_idx, w.keys, a.T, a.N,
