@@ -280,10 +280,6 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
                 s[0][r] = fmaf(ks0, p0[r], s[0][r]);
                 s[1][r] = fmaf(ks1, p1[r], s[1][r]);
             }
-            // At most two blocks in flight: bounds the live partials and
-            // converted operands.
-            if (blk & 1)
-                __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- softmax over the tile ---------------------------------------
@@ -359,7 +355,6 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
                         o[t] = mfma16(va, wlo, o[t]);
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
         wave_lds_sync();  // LDS reads done before the next tile's copies
