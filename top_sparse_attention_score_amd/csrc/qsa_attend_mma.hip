@@ -62,7 +62,9 @@ namespace qsa {
 constexpr int kMmaWaves = 4;      // (token, chunk) items per workgroup
 
 // SHQ: the four waves of the workgroup are chunks of one token and share the
-// split query through LDS (requires P % 4 == 0).
+// split query through LDS (requires P % 4 == 0).  With the query in LDS, or
+// fp16 queries (no lo half) in registers, the kernel fits 256 registers and
+// runs two waves per SIMD; fp32 queries in registers need one wave per SIMD.
 template <int G, int D, bool QF16, bool SHQ>
 __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_attend_mma(
     const void* __restrict__ q, const int8_t* __restrict__ Kq, const uint8_t* __restrict__ Ksc,
