@@ -327,3 +327,32 @@ def test_graph_replay_matches_eager(orc):
         assert torch.equal(path.ids, ids), rep
         step(None)                      # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", ["all_equal", "few_values"])
+def test_chip_wide_select_ties(orc, case):
+    """Rows longer than 65536 cells take the chip-wide select.  With every
+    score equal (q_idx = 0) the threshold bin holds all cells and the pivot
+    kernel streams the keys (more candidates than its list); with scores
+    from a few distinct values the threshold bin is a large exact tie.
+    Both must give the lowest-index rule bit for bit."""
+    cfg = dict(T=2, N=70000, di=64, k=2048, dense_max=2051, Hq=4, Hkv=1, D=64, P=4,
+               q_dtype="f32", out_dtype="f32", heavy_tail=False)
+    inp = make_inputs(cfg, seed=101, batch=2)
+    if case == "all_equal":
+        inp["q_idx"][:] = 0
+    else:
+        rng = np.random.default_rng(102)
+        vals = np.array([-1.0, 0.0, 0.5, 2.0], np.float16)
+        inp["K_idx"][:] = 0
+        inp["K_idx"][..., 0] = vals[rng.integers(0, 4, size=inp["K_idx"].shape[:2])]
+        inp["q_idx"][:] = 0
+        inp["q_idx"][..., 0] = 1.0
+    say(f"[chip-wide select] {case}")
+    res = run_gpu(inp)
+    ref = _oracle_all(orc, inp, inp["P"])
+    assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+    assert_out_close(res["out"], ref["out"])
+    if case == "all_equal":
+        for t in range(inp["T"]):
+            assert np.array_equal(res["ids"][:, t, :2048], np.tile(np.arange(2048), (2, 1)))
