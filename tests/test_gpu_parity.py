@@ -356,3 +356,30 @@ def test_chip_wide_select_ties(orc, case):
     if case == "all_equal":
         for t in range(inp["T"]):
             assert np.array_equal(res["ids"][:, t, :2048], np.tile(np.arange(2048), (2, 1)))
+
+
+@pytest.mark.parametrize("cfg,batch", [("decode", 256), ("draft", 32), ("long", 16)])
+def test_bench_launch_configuration(orc, cfg, batch):
+    """The batch sizes bench.py times, built the way it builds them (a few
+    distinct seeded problems tiled over the batch): every replica's ids equal
+    its problem's oracle ids bit for bit and its output is within tolerance."""
+    import top_sparse_attention_score_amd as qsa
+    nd = min(4, batch)
+    base = make_inputs(cfg, seed=103, batch=nd)
+    reps = batch // nd
+    dev = {}
+    for key in ("q_idx", "K_idx", "q", "Kq", "Ksc", "Vq", "Vsc"):
+        t = torch.from_numpy(base[key]).cuda()
+        dev[key] = t.repeat((reps,) + (1,) * (t.dim() - 1)).contiguous()
+    inp = dict(base)
+    inp["batch"] = batch
+    say(f"[bench config] {cfg} B={batch} ({nd} distinct problems)")
+    path = qsa.path_for(inp)
+    path.run(dev)
+    torch.cuda.synchronize()
+    ref = _oracle_all(orc, base, base["P"])
+    ids, n_sel, out = path.ids.cpu().numpy(), path.n_sel.cpu().numpy(), path.out.cpu().numpy()
+    for b in range(batch):
+        d = b % nd
+        assert_ids_equal(ids[b], n_sel[b], ref["ids"][d], ref["n_sel"][d])
+        assert_out_close(out[b], ref["out"][d], f"replica {b}")
