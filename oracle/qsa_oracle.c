@@ -74,6 +74,8 @@ uint16_t qo_double_to_half(double x)
     const uint16_t sign = signbit(x) ? 0x8000u : 0u;
     if (isnan(x))
         return 0x7e00u;
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7c00u);            /* infinity stays infinity */
     const double a = fabs(x);
     if (a < ldexp(1.0, -14)) {
         /* subnormal range: the quantum is 2^-24 */

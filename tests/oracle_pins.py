@@ -91,7 +91,8 @@ def pin_half_encode(orc):
     xs = [mids[sel], finite[rng.choice(finite.size, 2000, replace=False)],
           rng.standard_normal(3000) * 10.0 ** rng.integers(-9, 6, size=3000),
           np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 7e4, -7e4, 2.0 ** -24,
-                    2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -14, 6.1e-5])]
+                    2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -14, 6.1e-5,
+                    np.inf, -np.inf, 1e300, -1e300])]
     x = np.concatenate(xs)
     with np.errstate(over="ignore"):
         ref = x.astype(np.float16).view(np.uint16)
