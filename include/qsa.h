@@ -97,10 +97,16 @@ QSA_API int qsa_version(void);
  *   ws     device scratch of at least qsa_index_topk_workspace(desc) bytes,
  *          16-byte aligned; its contents on entry do not matter.
  *
- * Selection is exact on fp32 scores: ids equal a full sort by (score desc,
- * index asc) of the fp32 scores.  With index inputs on a grid where fp32
- * accumulation is exact (e.g. multiples of 2^-5 in [-4, 4] with d_idx <=
- * 1024) this is the exact-arithmetic selection.
+ * Selection is exact on the fp32 scores the kernels compute: ids equal a
+ * full sort by (score desc, index asc) of those scores.  Each fp32 score is
+ * the sum of the exact fp16 x fp16 products, rounded in an order that
+ * depends on the kernel variant (one token per call, 2..16 tokens, more),
+ * so it is within gamma_d * sum_i |q_i k_i| of the exact score (gamma_d =
+ * d u / (1 - d u), u = 2^-24, d = d_idx).  A kept id can therefore differ
+ * from the exact-arithmetic selection only for cells whose exact score lies
+ * within 2 gamma_d max_j sum_i |q_i k_ji| of the k-th exact score.  Where
+ * every partial sum is exact in fp32 (e.g. inputs that are multiples of
+ * 2^-5 in [-4, 4] with d_idx <= 1024) the selection is the exact one.
  *
  * Supported: d_idx in {64, 128}; 1 <= k <= ids_cap; 0 <= dense_max <=
  * ids_cap; 0 <= pos0; pos0 + T <= N <= 2^22; 1 <= batch*T <= 65535.
@@ -132,17 +138,21 @@ QSA_API int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const 
  * and head h, with x_j = scale * sum_d q[h][d] * Kq[j][g][d] * Ksc[j][g][d/32]:
  *   m = max_j x_j,   l = sum_j exp(x_j - m),
  *   o[d] = sum_j exp(x_j - m) * Vq[j][g][d] * Vsc[j][g][d/32]   (unnormalised)
- * An empty chunk gives m = -inf, l = 0, o = 0.
+ * An empty chunk gives m = -inf, l = 0, o = 0.  scale = desc->scale, or
+ * 1/sqrt(D) when desc->scale is 0 (no scale is stated by the pages; the
+ * usual softmax-attention scale is the default).
  *
  * Arithmetic.  QSA_ATTEND_VECTOR evaluates the definition with fp32 FMAs.
  * QSA_ATTEND_MATRIX (the default) runs both products on the matrix cores
  * with fp16 operands that carry the fp32 values: int8 codes are exact in
  * fp16; an fp32 query element and each weight exp(x_j - m) * Vsc are split
  * into two fp16 halves (hi + lo, 22 significant bits) whose products
- * accumulate in fp32.  Its results agree with the fp32 definition to
- * within about 1e-6 relative to the output scale.  It requires finite
- * |q| < 65504 and |Vsc| < 255 (larger values overflow the fp16 halves and
- * give non-finite output); fp16 queries are used as given.
+ * accumulate in fp32.  Exact power-of-two shifts (per item for the query,
+ * per 32-cell tile for weight x V scale) keep both halves finite and normal
+ * for any finite query and any finite fp16 scale, so the results agree
+ * with the fp32 definition to within about 1e-6 relative to the output
+ * scale over the whole value range (tested from fp16-subnormal scales to
+ * 8000 and |q| up to 1e5).  fp16 queries are used as given.
  *
  * Inputs
  *   q      [B][T][Hq][D], fp32 (q_dtype QSA_F32) or fp16 (QSA_F16), 16-byte
@@ -179,7 +189,7 @@ typedef struct qsa_attn_desc {
     int P;               /* split-KV chunks per token */
     int ids_cap;         /* row length of ids */
     int n_cells;         /* N, cells per problem (sizes the default batch strides) */
-    float scale;         /* softmax scale, e.g. 1/sqrt(D) */
+    float scale;         /* softmax scale; 0 selects the default 1/sqrt(D) */
     int q_dtype;         /* qsa_dtype of q */
     int out_dtype;       /* qsa_dtype of the merged output */
     int algo;            /* qsa_attend_algo; 0 (zero-initialised) = default */

@@ -82,7 +82,7 @@ int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
     L->P = d->P;
     L->cap = d->ids_cap;
     L->N = d->n_cells;
-    L->scale = d->scale;
+    L->scale = d->scale != 0.f ? d->scale : 1.f / sqrtf((float)d->D);
     L->q_f16 = d->q_dtype == QSA_F16;
     L->out_f16 = d->out_dtype == QSA_F16;
     L->algo = d->algo;

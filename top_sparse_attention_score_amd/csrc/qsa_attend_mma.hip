@@ -18,8 +18,14 @@
 //   - a softmax weight times a V scale is split the same way (hi rounded
 //     toward zero, so x - hi is exact), the weight carried at 2^4 times its
 //     value so the lo half stays clear of the fp16 subnormal range.
-// fp16 products are exact in fp32, so the remaining error is fp32
-// accumulation order plus the 2^-22 split residue.
+// Two exact power-of-two shifts keep every half finite and normal whatever
+// the magnitudes: an item's fp32 query is split as q * 2^-eq with its
+// largest |q| in [2^14, 2^15) (the logits are scaled back by 2^eq), and a
+// tile's weight x scale operands carry 2^ev with the tile's largest V scale
+// in [2^6, 2^7) (the accumulated output is rescaled when ev changes from
+// tile to tile, and scaled back at the end).  fp16 products are exact in
+// fp32, so the remaining error is fp32 accumulation order plus the 2^-22
+// split residue.
 //
 // Mapping (one wave per (token, chunk) item, four items of one KV head per
 // workgroup; a tile is 32 consecutive kept cells):
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
     __shared__ __align__(16) uint32_t vsc_all[kMmaWaves][SROWS * TC];
     __shared__ __align__(16) float p_all[kMmaWaves][16 * PP];
     __shared__ __align__(16) half8_t q_all[SHQ ? QH * NB * 64 : 1];
+    __shared__ float s_qmax[kMmaWaves];
 
     // Workgroup w serves KV head g = (w / 8) % Hkv of item group
     // (w / (8 Hkv)) * 8 + w % 8: the groups' KV heads are 8 workgroup ids
@@ -104,14 +111,26 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
     if (group * kMmaWaves >= (long long)BT * P)
         return;  // grid padding (whole workgroup)
 
+    int eq = 0;  // fp32 queries are split as q * 2^-eq (see the header)
     if constexpr (SHQ) {
         // Every wave of the block has the same token (P % 4 == 0 and the grid
         // covers whole blocks of items); each builds some query blocks.
         const int bt0 = (int)((group * kMmaWaves) / P);
         const size_t prow0 = (size_t)bt0 * Hq + (size_t)g * G;
+        if constexpr (!QF16) {
+            float amax = 0.f;
+            for (int blk = wave; blk < NB; blk += kMmaWaves)
+                amax = fmaxf(amax, q_block_absmax<G, D>(q, prow0, hq, q4, blk));
+            amax = wave_max16x4(amax);
+            if (lane == 0)
+                s_qmax[wave] = amax;
+            __syncthreads();
+            amax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
+            eq = pow2_shift(amax, kQShiftLo);
+        }
         for (int blk = wave; blk < NB; blk += kMmaWaves) {
             half8_t hi, lo;
-            load_q_block<G, D, QF16>(q, prow0, hq, q4, blk, hi, lo);
+            load_q_block<G, D, QF16>(q, prow0, hq, q4, blk, eq, hi, lo);
             q_all[(QH * blk) * 64 + lane] = hi;
             if constexpr (!QF16)
                 q_all[(QH * blk + 1) * 64 + lane] = lo;
@@ -146,10 +165,18 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
 
     half8_t qh[SHQ ? 1 : NB], ql[SHQ ? 1 : NB];
     if constexpr (!SHQ) {
+        if constexpr (!QF16) {
+            float amax = 0.f;
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+                amax = fmaxf(amax, q_block_absmax<G, D>(q, prow, hq, q4, blk));
+            eq = pow2_shift(wave_max16x4(amax), kQShiftLo);
+        }
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk)
-            load_q_block<G, D, QF16>(q, prow, hq, q4, blk, qh[blk], ql[blk]);
+            load_q_block<G, D, QF16>(q, prow, hq, q4, blk, eq, qh[blk], ql[blk]);
     }
+    const float scale_q = __builtin_amdgcn_ldexpf(scale, eq);  // logit scale of the split query
 
     const char* Kb = (const char*)Kq + (long long)b * kq_bs + (long long)g * D + 8 * q4;
     const char* Ksb = (const char*)Ksc + (long long)b * ksc_bs + (long long)g * NB * 2;
@@ -215,6 +242,7 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
     // Transpose-read base of this lane: cell 8*q4 + hq/2 of the [chunk][cell]
     // table, 8-byte half hq&1; slice t adds 512*t.
     const int8_t* v_rd = v_s + 16 * (8 * q4 + (hq >> 1)) + 8 * (hq & 1);
+    int ev = 0;  // the accumulated output carries 2^ev (see the header)
 
 #pragma unroll 1
     for (;;) {
@@ -289,8 +317,8 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
             const bool v0 = hq < nt, v1 = 16 + hq < nt;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float x0 = v0 ? s[0][r] * scale : -INFINITY;
-                const float x1 = v1 ? s[1][r] * scale : -INFINITY;
+                const float x0 = v0 ? s[0][r] * scale_q : -INFINITY;
+                const float x1 = v1 ? s[1][r] * scale_q : -INFINITY;
                 m_run[r] = fmaxf(m_run[r], row16_max(fmaxf(x0, x1)));
                 // Move the reference max only when the running max exceeds
                 // it by more than kLazyMax (always on the first tile).
@@ -320,16 +348,31 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
 
         // ---- PV on the matrix cores: O^T[d][h] += V^T[d][cell] W[cell][h] --
         {
+            // Shift of this tile from its largest V scale (tail cells repeat
+            // the first cell, so they do not change the max).
+            uint32_t smax = 0;
+#pragma unroll
+            for (int i = 0; i < SROWS * TC / 64; ++i) {
+                const uint32_t w = vsc_s[64 * i + lane];
+                smax = max(smax, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
+            }
+            const float vmax = wave_max16x4(half_bits_to_float((uint16_t)smax));
+            const int ev_t = vmax > 0.f ? -pow2_shift(vmax, kVShiftLo) : ev;
+            const int dev = (t0 == beg) ? 0 : ev_t - ev;
+            ev = ev_t;
             const float* pr_s = p_s + hq * PP;
             const float4 pa = *(const float4*)(pr_s + 8 * q4);
             const float4 pb = *(const float4*)(pr_s + 8 * q4 + 4);
-            const float alpha = pr_s[32];
+            const float alpha = __builtin_amdgcn_ldexpf(pr_s[32], dev);
             if (t0 != beg && __ballot(alpha != 1.f)) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
                     o[t] *= alpha;
             }
-            const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pw[e] = __builtin_amdgcn_ldexpf(pw[e], ev);
 #pragma unroll
             for (int pr = 0; pr < NPR; ++pr) {
                 const uint4 sa = *(const uint4*)(vsc_s + pr * TC + 8 * q4);
@@ -382,7 +425,7 @@ __global__ __launch_bounds__(64 * kMmaWaves, (SHQ || QF16) ? 2 : 1) void k_atten
     }
     wave_lds_sync();
     if (hq < G) {
-        const float f = p_s[hq * PP + 33] * (1.f / kWScale);
+        const float f = __builtin_amdgcn_ldexpf(p_s[hq * PP + 33] * (1.f / kWScale), -ev);
         float* dst = po + ((prow + hq) * P + c) * D + 4 * q4;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {

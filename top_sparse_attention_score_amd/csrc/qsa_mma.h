@@ -13,6 +13,12 @@ typedef __attribute__((address_space(3))) int2v_t lds_int2v_t;
 constexpr int kMmaCells = 32;     // cells per tile
 constexpr float kWScale = 16.f;   // weights are carried at 2^4 times their value
 constexpr float kLazyMax = 2.7f;  // reference max slack (natural log units, < ln 16)
+// Query shift target: the largest |q| of an item is carried in [2^14, 2^15).
+constexpr int kQShiftLo = 14;
+// V-scale shift target: the largest V scale of a tile is carried in
+// [2^6, 2^7), so weight (<= e^kLazyMax < 15) x kWScale x scale < 2^15 stays
+// finite in fp16 and the lo half of every large term stays normal.
+constexpr int kVShiftLo = 6;
 
 __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c)
 {
@@ -93,11 +99,50 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
+// Largest |x| of this lane's eight fp32 query elements of block blk (head
+// hq, elements 32*blk + 8*q4 .. +7; 0 for the padded heads hq >= G).
+template <int G, int D>
+__device__ __forceinline__ float q_block_absmax(const void* q, size_t prow, int hq, int q4,
+                                                int blk)
+{
+    if (hq >= G)
+        return 0.f;
+    const float4* qr = (const float4*)((const float*)q + (prow + hq) * D + 32 * blk + 8 * q4);
+    const float4 a = qr[0], b = qr[1];
+    return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                 fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+}
+
+// Power-of-two shift e that brings a positive finite amax into [2^lo, 2^(lo+1))
+// as amax * 2^-e (0 for amax = 0, infinite or NaN).
+__device__ __forceinline__ int pow2_shift(float amax, int lo)
+{
+    if (!(amax > 0.f) || amax == __builtin_inff())
+        return 0;
+    return __builtin_amdgcn_frexp_expf(amax) - 1 - lo;  // floor(log2 amax) - lo
+}
+
+// Wave-wide max (every lane gets it): DPP within rows of 16, then the four
+// row results.
+__device__ __forceinline__ float wave_max16x4(float v)
+{
+    v = row16_max(v);
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // The query operand of block blk for this lane: head hq (zero beyond G),
-// elements 32*blk + 8*q4 .. +7, as fp16 hi and lo halves.
+// elements 32*blk + 8*q4 .. +7, as fp16 hi and lo halves of x * 2^-eq
+// (fp32 queries; the exact power-of-two shift keeps both halves normal and
+// finite, and the logits are scaled back by 2^eq).  fp16 queries are used
+// as given (eq ignored).
 template <int G, int D, bool QF16>
 __device__ __forceinline__ void load_q_block(const void* q, size_t prow, int hq, int q4, int blk,
-                                             half8_t& hi, half8_t& lo)
+                                             int eq, half8_t& hi, half8_t& lo)
 {
     const bool hv = hq < G;
     const size_t off = (prow + (hv ? hq : 0)) * D + 32 * blk + 8 * q4;
@@ -111,8 +156,9 @@ __device__ __forceinline__ void load_q_block(const void* q, size_t prow, int hq,
         const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const _Float16 h = (_Float16)x[e];
-            const _Float16 l = (_Float16)(x[e] - (float)h);
+            const float xs = __builtin_amdgcn_ldexpf(x[e], -eq);
+            const _Float16 h = (_Float16)xs;
+            const _Float16 l = (_Float16)(xs - (float)h);
             hi[e] = hv ? h : (_Float16)0.f;
             lo[e] = hv ? l : (_Float16)0.f;
         }

@@ -9,7 +9,6 @@ call is rejected, a QsaError is raised.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -123,8 +122,9 @@ def attn_desc(*, batch: int, T: int, Hq: int, Hkv: int, D: int, P: int, ids_cap:
               out_dtype: int = QSA_F32, strides: dict | None = None,
               algo: int = 0) -> AttnDesc:
     """Attention descriptor; `strides` may set any of the *_cell_stride /
-    *_batch_stride fields (bytes); unset ones keep the dense default."""
-    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    *_batch_stride fields (bytes); unset ones keep the dense default.
+    scale None passes 0, for which the library uses its default."""
+    sc = 0.0 if scale is None else float(scale)
     d = AttnDesc(batch, T, Hq, Hkv, D, P, ids_cap, n_cells, sc, q_dtype, out_dtype, algo)
     for key, val in (strides or {}).items():
         setattr(d, key, int(val))
