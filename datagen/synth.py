@@ -7,7 +7,10 @@ public dataset is involved.  These generators produce inputs of the same
 shapes and kinds:
 
 * index queries and keys: N(0,1) rounded to the 2^-5 grid and clamped to
-  [-4, 4], stored as fp16 (every such value is exact in fp16).  On this grid
+  [-4, 4], stored as fp16 (every such value is exact in fp16).  With
+  ``index_grid=False`` they are N(0,1) rounded to the nearest fp16 instead
+  (general fp16 keys, where fp32 score sums depend on the summation order).
+  On the grid
   every fp16 x fp16 product is a multiple of 2^-10 of magnitude <= 16, so every
   partial sum of up to 1024 such products is a multiple of 2^-10 below 2^14 and
   is exact in fp32 (24-bit significand): scores computed in fp32 in any
@@ -69,6 +72,11 @@ def _grid16(x: np.ndarray) -> np.ndarray:
     return np.clip(np.round(x * 32.0) / 32.0, -4.0, 4.0).astype(np.float16)
 
 
+def _raw16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest fp16 (no grid)."""
+    return x.astype(np.float16)
+
+
 def _kv(rng: np.random.Generator, B: int, N: int, Hkv: int, D: int):
     z = rng.standard_normal((B, N, Hkv, D), dtype=np.float32)
     codes = np.clip(np.rint(z * 36.0), -127, 127).astype(np.int8)
@@ -87,9 +95,10 @@ def make_inputs(cfg="decode", *, seed: int = 1000, batch: int = 1, **over) -> di
     p.setdefault("cap", max(p["k"], p["dense_max"]))
     B = batch
     rng = np.random.default_rng(seed)
+    to16 = _grid16 if p.get("index_grid", True) else _raw16
 
     q_idx_f = rng.standard_normal((B, T, di))
-    q_idx = _grid16(q_idx_f)
+    q_idx = to16(q_idx_f)
     K_raw = rng.standard_normal((B, N, di))
     if p.get("heavy_tail"):
         for b in range(B):
@@ -97,7 +106,7 @@ def make_inputs(cfg="decode", *, seed: int = 1000, batch: int = 1, **over) -> di
             q_hat = qv / max(np.linalg.norm(qv), 1e-30)
             mask = rng.random(N) < 0.05
             K_raw[b, mask] += 3.0 * q_hat
-            K_b = _grid16(K_raw[b])
+            K_b = to16(K_raw[b])
             planted = np.flatnonzero(mask)
             if planted.size >= 2:
                 n_copy = max(1, planted.size // 100)
@@ -105,7 +114,7 @@ def make_inputs(cfg="decode", *, seed: int = 1000, batch: int = 1, **over) -> di
                 src = rng.choice(planted, size=n_copy, replace=True)
                 K_b[dst] = K_b[src]
             K_raw[b] = K_b.astype(np.float64)
-    K_idx = _grid16(K_raw)
+    K_idx = to16(K_raw)
 
     if p["q_dtype"] == "f16":
         q = rng.standard_normal((B, T, Hq, D), dtype=np.float32).astype(np.float16)
