@@ -11,6 +11,7 @@ import torch
 from datagen import make_inputs, scattered_ids, sweep_cases
 from tests.gpu_util import (assert_ids_equal, assert_out_close, assert_partials_close,
                             run_gpu, say)
+from tests.oracle_pool import host_threads, oracle_all_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -40,37 +41,34 @@ def test_workload_parity(orc, cfg, batch, algo):
     assert_out_close(res["out"], ref["out"])
 
 
+_PROMPT_REF = {}
+
+
+def _prompt_reference(orc, inp):
+    """The oracle's ids and output for all 2048 tokens of the prompt chunk
+    (computed once per module, in parallel slices on the host cores)."""
+    if "ref" not in _PROMPT_REF:
+        say(f"[parity] prompt: oracle over all {inp['T']} tokens on {host_threads()} threads")
+        _PROMPT_REF["ref"] = oracle_all_tokens(orc, inp, P=1,
+                                               scale=1.0 / math.sqrt(inp["D"]))
+    return _PROMPT_REF["ref"]
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("algo", ["matrix", "vector"])
-def test_prompt_chunk_sampled(orc, algo):
-    """The 2048-token prompt chunk at full size on the GPU; the oracle checks
-    sampled tokens one by one, and every token's kept set is checked against
-    exact float64 scores (a property that holds at any size)."""
+def test_prompt_chunk_full(orc, algo):
+    """The 2048-token prompt chunk at full size on the GPU against the
+    oracle on every token: ids and n_sel bit for bit, the fp16 output of
+    every token within tolerance."""
     inp = make_inputs("prompt", seed=1005)
     say(f"[parity] prompt T=2048 N=65536 full size {algo}")
     res = run_gpu(inp, algo=algo)
-    T, pos0, k = inp["T"], inp["pos0"], inp["k"]
-    assert np.all(res["n_sel"] == k)
-    S = inp["q_idx"][0].astype(np.float64) @ inp["K_idx"][0].astype(np.float64).T
-    for t in range(T):
-        nvis = pos0 + t + 1
-        kept = res["ids"][0, t, :k]
-        assert np.all(np.diff(kept) > 0) and kept[0] >= 0 and kept[-1] < nvis
-        assert np.all(res["ids"][0, t, k:] == -1)
-        s = S[t, :nvis]
-        mask = np.zeros(nvis, bool)
-        mask[kept] = True
-        lo = s[mask].min()
-        assert s[~mask].max() <= lo, t
-        tie_out = np.flatnonzero(~mask & (s == lo))
-        if tie_out.size:
-            assert np.flatnonzero(mask & (s == lo)).max() < tie_out.min(), t
-    for t in (0, 1, 777, 1500, 2046, 2047):
-        one = dict(inp)
-        one.update(T=1, pos0=pos0 + t, q_idx=inp["q_idx"][:, t:t + 1], q=inp["q"][:, t:t + 1])
-        ref = _oracle_all(orc, one, 1)
-        assert_ids_equal(res["ids"][:, t:t + 1], res["n_sel"][:, t:t + 1], ref["ids"],
-                         ref["n_sel"])
-        assert_out_close(res["out"][:, t:t + 1], ref["out"], f"token {t}")
+    ref = _prompt_reference(orc, inp)
+    assert_ids_equal(res["ids"], res["n_sel"], ref["ids"], ref["n_sel"])
+    assert_out_close(res["out"], ref["out"], "prompt chunk, all tokens")
+    worst = max(float(np.abs(res["out"][:, t].astype(np.float64) - ref["out"][:, t]).max())
+                for t in range(inp["T"]))
+    say(f"[parity] prompt {algo}: worst token max-abs error {worst:.3e}")
 
 
 def test_pos_sweep(orc):
