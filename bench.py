@@ -111,30 +111,73 @@ def profiled_traffic(workload: str, B: int, P: int, algo: str):
         return None
 
 
-def cpu_baseline(inp_cfg: str, target_s: float, P: int) -> dict:
-    """The oracle (plain C, double, one thread) on as many problems of the same
-    workload as fit in about target_s seconds."""
+def host_record() -> dict:
+    """CPU model, logical CPUs and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return dict(cpu_model=model, nproc=os.cpu_count(), usable_cpus=usable)
+
+
+def _oracle_problem(orc, inp_cfg: str, i: int, P: int) -> tuple[int, float]:
+    """One sample problem of the workload through the oracle: (kept cells,
+    seconds spent in the oracle call)."""
     from datagen import make_inputs
+    inp = make_inputs(inp_cfg, seed=9000 + i, batch=1)
+    if inp_cfg == "prompt":   # one token of the chunk per sample
+        t = i % inp["T"]
+        inp.update(T=1, pos0=inp["pos0"] + t, q_idx=inp["q_idx"][:, t:t + 1],
+                   q=inp["q"][:, t:t + 1])
+    t0 = time.perf_counter()
+    r = orc.run(inp, P=P, scale=1.0 / math.sqrt(inp["D"]))
+    return int(r["n_sel"].sum()), time.perf_counter() - t0
+
+
+def cpu_baseline(inp_cfg: str, target_s: float, P: int) -> dict:
+    """The oracle (plain C, double) on as many problems of the same workload
+    as fit in about target_s seconds of oracle time on one thread (the
+    reported value); then the same on every usable host CPU (up to 16), one
+    thread each, for about half that time (reported beside it as the sum of
+    the threads' rates).  Only the oracle calls are timed, not the input
+    generation."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle.oracle import default
     orc = default()
     done, cells, t_used = 0, 0, 0.0
-    seed = 9000
     while t_used < target_s:
-        inp = make_inputs(inp_cfg, seed=seed + done, batch=1)
-        if inp_cfg == "prompt":   # one token of the chunk per sample
-            t = done % inp["T"]
-            inp.update(T=1, pos0=inp["pos0"] + t, q_idx=inp["q_idx"][:, t:t + 1],
-                       q=inp["q"][:, t:t + 1])
-        t0 = time.perf_counter()
-        r = orc.run(inp, P=P, scale=1.0 / math.sqrt(inp["D"]))
-        t_used += time.perf_counter() - t0
-        cells += int(r["n_sel"].sum())
+        c, dt = _oracle_problem(orc, inp_cfg, done, P)
+        cells += c
+        t_used += dt
         done += 1
-    unit = "cells/s"
     what = "token" if inp_cfg == "prompt" else "problem"
-    return dict(value=cells / t_used, unit=unit, cores=1, kind="oracle",
+    host = host_record()
+    threads = max(1, min(16, host["usable_cpus"] or 1))
+
+    def worker(w):
+        n, c_w, t_w = 0, 0, 0.0
+        while t_w < target_s / 2:
+            c, dt = _oracle_problem(orc, inp_cfg, 10000 + 1000 * w + n, P)
+            c_w, t_w, n = c_w + c, t_w + dt, n + 1
+        return n, c_w / t_w
+
+    with ThreadPoolExecutor(threads) as ex:
+        per = list(ex.map(worker, range(threads)))
+    return dict(value=cells / t_used, unit="cells/s", cores=1, kind="oracle",
                 sample=f"{done} {what}(s) of the {inp_cfg} workload, index+attend+merge, "
-                       f"{t_used:.1f} s single-threaded")
+                       f"{t_used:.1f} s of oracle time on one thread",
+                host=host,
+                all_cores=dict(value=sum(r for _, r in per), threads=threads,
+                               sample=f"{sum(n for n, _ in per)} {what}(s) on {threads} "
+                                      f"threads, ~{target_s / 2:.0f} s of oracle time each"))
 
 
 def single_problem_latency(qsa, base: dict, P: int, algo_code: int, steps: int = 50) -> dict:
@@ -287,6 +330,7 @@ def main() -> None:
             stage[i] += e[i].elapsed_time(e[i + 1])
     stage_ms = stage / K
     step_ms = float(evs[0][0].elapsed_time(evs[-1][4])) / K
+    per_step_us = np.array([e[0].elapsed_time(e[4]) * 1e3 for e in evs])
 
     n_sel_total = int(path.n_sel.sum().item())
     by = algorithmic_bytes(inp, B, n_sel_total)
@@ -333,6 +377,10 @@ def main() -> None:
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": by["total"],
         "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(names, stage_ms)},
+        "step_us": {"mean": round(step_ms * 1e3, 2),
+                    "median": round(float(np.median(per_step_us)), 2),
+                    "min": round(float(per_step_us.min()), 2),
+                    "max": round(float(per_step_us.max()), 2)},
         "wall_s": round(wall, 3),
         "roofline": roof,
     }
