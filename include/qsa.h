@@ -129,6 +129,30 @@ QSA_API int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const 
                    void* stream);
 
 /* ------------------------------------------------------------------------
+ * qsa_index_topk_noalloc -- qsa_index_topk without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops and harnesses that forbid allocation).
+ *
+ * The workspace is a fixed array of QSA_NOALLOC_WORKSPACE_BYTES in device
+ * memory inside the library, one per GPU, held by that GPU until the
+ * process ends; its address on a device is looked up once, on the first
+ * call on that device.  The call allocates nothing.  Inputs, outputs,
+ * results and errors are those of qsa_index_topk; a shape whose
+ * qsa_index_topk_workspace(desc) exceeds QSA_NOALLOC_WORKSPACE_BYTES
+ * returns QSA_ERR_WORKSPACE and enqueues nothing.
+ *
+ * Every call on one GPU uses that GPU's one array, and the kernels leave
+ * their intermediate data in it: calls that overlap on one GPU (from several
+ * streams or threads without ordering between them) race and give undefined
+ * results.  Calls ordered on one stream are safe.
+ * --------------------------------------------------------------------- */
+#define QSA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+QSA_API int qsa_index_topk_noalloc(const qsa_index_desc* desc, const void* q_idx,
+                                   const void* K_idx, int32_t* ids, int32_t* n_sel,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
  * qsa_attend -- split-KV attention partials over the kept cells
  * ("opus r20 ..." page, section 2, qsa_attn).
  *

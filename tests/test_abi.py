@@ -197,3 +197,17 @@ def test_append_pointer_checks():
     d.reserved = 1
     assert L.qsa_kv_append(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 16, 16, None) == INVALID
     assert L.qsa_kv_append(None, 16, 16, 16, 16, 16, 16, 16, 16, None) == INVALID
+
+
+def test_noalloc_index_host_checks():
+    """qsa_index_topk_noalloc validates like qsa_index_topk and rejects a
+    shape whose workspace exceeds its fixed array before touching the GPU."""
+    L = qb.lib()
+    assert L.qsa_index_topk_noalloc(None, 16, 16, 16, 16, None) == INVALID
+    assert L.qsa_index_topk_noalloc(ctypes.byref(_idesc(batch=0)), 16, 16, 16, 16, None) == INVALID
+    assert L.qsa_index_topk_noalloc(ctypes.byref(_idesc(d_idx=96)), 16, 16, 16, 16,
+                                    None) == UNSUPPORTED
+    assert L.qsa_index_topk_noalloc(ctypes.byref(_idesc()), None, 16, 16, 16, None) == INVALID
+    big = _idesc(T=2048, n_cells=65536, pos0=63488)
+    assert L.qsa_index_topk_workspace(ctypes.byref(big)) > qsa.QSA_NOALLOC_WORKSPACE_BYTES
+    assert L.qsa_index_topk_noalloc(ctypes.byref(big), 16, 16, 16, 16, None) == WORKSPACE

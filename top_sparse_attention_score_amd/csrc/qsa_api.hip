@@ -5,10 +5,49 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qsa.h"
 #include "qsa_launch.h"
 
+// Workspace of qsa_index_topk_noalloc: a fixed array in device memory, one
+// per GPU (each device that loads the library holds its own copy until the
+// process ends).  Host code never names it directly: the array's name is a
+// host-side stand-in, not a device address, so its address on each device is
+// taken once with hipGetSymbolAddress and kept in g_scratch below.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_WORKSPACE_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on device dev (made current for the lookup).
+hipError_t scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev)
+            e = hipSetDevice(dev);
+        void* p = nullptr;
+        if (e == hipSuccess)
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = e2;
+        }
+        g_scratch[dev] = (e == hipSuccess) ? p : nullptr;
+        g_scratch_err[dev] = e;
+    });
+    *out = g_scratch[dev];
+    return g_scratch_err[dev];
+}
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -150,6 +189,28 @@ int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const void* K_
     if (qsa::launch_index_topk(a, (hipStream_t)stream) != hipSuccess)
         return QSA_ERR_HIP;
     return QSA_OK;
+}
+
+int qsa_index_topk_noalloc(const qsa_index_desc* desc, const void* q_idx, const void* K_idx,
+                           int32_t* ids, int32_t* n_sel, void* stream)
+{
+    const int st = check_index(desc);
+    if (st != QSA_OK)
+        return st;
+    if (!q_idx || !K_idx || !ids || !n_sel)
+        return QSA_ERR_INVALID_ARG;
+    const size_t need = qsa::index_workspace_bytes(desc->batch, desc->T, desc->n_cells);
+    if (need > (size_t)QSA_NOALLOC_WORKSPACE_BYTES)
+        return QSA_ERR_WORKSPACE;
+    int dev = -1;
+    const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return QSA_ERR_HIP;
+    void* ws = nullptr;
+    if (scratch_address(dev, &ws) != hipSuccess || !ws)
+        return QSA_ERR_HIP;
+    return qsa_index_topk(desc, q_idx, K_idx, ids, n_sel, ws, (size_t)QSA_NOALLOC_WORKSPACE_BYTES,
+                          stream);
 }
 
 size_t qsa_partials_floats(const qsa_attn_desc* desc)

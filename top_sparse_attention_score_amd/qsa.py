@@ -22,6 +22,8 @@ QSA_F16 = 1
 QSA_ATTEND_AUTO = 0
 QSA_ATTEND_MATRIX = 1
 QSA_ATTEND_VECTOR = 2
+# bytes of the fixed workspace of qsa_index_topk_noalloc (include/qsa.h)
+QSA_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 _c_int, _c_ll, _c_float, _vp = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p
 
@@ -73,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.qsa_index_topk.argtypes = [ctypes.POINTER(IndexDesc), _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp]
         L.qsa_index_topk.restype = _c_int
+        L.qsa_index_topk_noalloc.argtypes = [ctypes.POINTER(IndexDesc), _vp, _vp, _vp, _vp,
+                                             _vp]
+        L.qsa_index_topk_noalloc.restype = _c_int
         L.qsa_partials_floats.argtypes = [ctypes.POINTER(AttnDesc)]
         L.qsa_partials_floats.restype = ctypes.c_size_t
         L.qsa_attend.argtypes = [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -154,6 +159,11 @@ def qsa_index_topk(desc: IndexDesc, q_idx, K_idx, ids, n_sel, ws, stream=None) -
     _check(lib().qsa_index_topk(ctypes.byref(desc), _ptr(q_idx), _ptr(K_idx), _ptr(ids),
                                 _ptr(n_sel), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "qsa_index_topk")
+
+
+def qsa_index_topk_noalloc(desc: IndexDesc, q_idx, K_idx, ids, n_sel, stream=None) -> None:
+    _check(lib().qsa_index_topk_noalloc(ctypes.byref(desc), _ptr(q_idx), _ptr(K_idx), _ptr(ids),
+                                        _ptr(n_sel), _stream(stream)), "qsa_index_topk_noalloc")
 
 
 def qsa_attend(desc: AttnDesc, q, Kq, Ksc, Vq, Vsc, ids, n_sel, partials,
