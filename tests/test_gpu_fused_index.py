@@ -1,0 +1,110 @@
+"""The many-token index path (more than 16 tokens against rows of 16384 to
+65536 cells) that never writes the score matrix: a sampled lower bound for
+each token's k-th largest key, a score GEMM that keeps only the cells at or
+above it, and an exact select among those candidates, with a whole-row
+fallback for tokens whose candidate list cannot prove the selection (fewer
+than k candidates, or more than the list holds).  Ids and n_sel must equal
+the oracle's bit for bit on grid inputs, on the normal path and on both
+fallbacks."""
+import numpy as np
+import pytest
+import torch
+
+import top_sparse_attention_score_amd as qsa
+from datagen import make_inputs
+from tests.gpu_util import assert_ids_equal, say
+from tests.oracle_pool import host_threads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def _gpu_ids(inp):
+    path = qsa.path_for(inp)
+    dev = qsa.to_device(inp)
+    path.index(dev["q_idx"], dev["K_idx"])
+    torch.cuda.synchronize()
+    return path.ids.cpu().numpy(), path.n_sel.cpu().numpy()
+
+
+def _oracle_ids(orc, inp, slice_tokens=8):
+    """The oracle's ids over token slices on the host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, T = inp["q_idx"].shape[:2]
+    ids = np.empty((B, T, inp["cap"]), np.int32)
+    ns = np.empty((B, T), np.int32)
+
+    def one(job):
+        b, t0 = job
+        t1 = min(T, t0 + slice_tokens)
+        i, n = orc.index_topk(inp["q_idx"][b:b + 1, t0:t1], inp["K_idx"][b:b + 1], k=inp["k"],
+                              pos0=inp["pos0"] + t0, dense_max=inp["dense_max"], cap=inp["cap"])
+        ids[b, t0:t1], ns[b, t0:t1] = i[0], n[0]
+
+    with ThreadPoolExecutor(host_threads()) as ex:
+        list(ex.map(one, [(b, t0) for b in range(B) for t0 in range(0, T, slice_tokens)]))
+    return ids, ns
+
+
+@pytest.mark.parametrize("N,T,pos0,batch", [(65536, 256, 65280, 1), (65536, 128, 30000, 2),
+                                            (40000, 200, 39800, 1), (16384, 64, 16320, 2)])
+def test_fused_index_matches_oracle(orc, N, T, pos0, batch):
+    inp = make_inputs("prompt", seed=9300 + T, batch=batch, N=N, T=T, pos0=pos0)
+    say(f"[fused index] N={N} T={T} pos0={pos0} B={batch}")
+    ids, ns = _gpu_ids(inp)
+    r_ids, r_ns = _oracle_ids(orc, inp)
+    assert_ids_equal(ids, ns, r_ids, r_ns)
+
+
+def _sample_cells(span: int, n: int = 2048) -> np.ndarray:
+    """Cells the library samples for the candidate bound (spread evenly, a
+    hashed offset inside each stride), to plant a case that defeats it."""
+    stride = max(1, span // n)
+    s = np.arange(n, dtype=np.uint64)
+    off = (((s * 0x9E3779B1) & 0xFFFFFFFF) >> 16) % stride
+    return (s * stride + off).astype(np.int64)
+
+
+def test_fused_index_fallbacks(orc):
+    """Problem 0: tokens 0-15 have a zero index query (every score equal),
+    tokens 16-31 see scores from two values (half the row ties at the top):
+    their candidate lists overflow.  Problem 1: 1000 sampled cells are
+    planted above all others, so the sampled bound keeps fewer than k
+    candidates.  Problem 2: four score values, a large exact tie at the k-th
+    inside the candidate list.  Tokens 32-63 of problem 0 take the normal
+    path."""
+    N, T = 65536, 64
+    pos0 = N - T
+    inp = make_inputs("prompt", seed=9400, batch=3, N=N, T=T, pos0=pos0)
+    inp["q_idx"][0, :16] = 0
+    rng = np.random.default_rng(9401)
+    inp["q_idx"][0, 16:32] = 0
+    inp["q_idx"][0, 16:32, 0] = 1.0
+    inp["K_idx"][0, :, 0] = np.where(rng.random(N) < 0.5, 1.0, 0.0).astype(np.float16)
+    cells = _sample_cells(pos0 + T)
+    assert len(np.unique(cells)) == 2048 and cells[:1000].max() <= pos0
+    # 1000 of the sampled cells score above every other cell: the sample's
+    # ~100th largest key lies among them, so only ~100 cells reach the bound
+    inp["K_idx"][1] = np.clip(inp["K_idx"][1], -1, 1)
+    inp["q_idx"][1] = np.abs(inp["q_idx"][1])
+    planted = cells[:1000]
+    inp["K_idx"][1, planted] += np.float16(3.0)
+    # Problem 2: scores in {0, 1, 2, 3} (1% at 3, 3% at 2): the candidates
+    # (score >= 2, about 2600) fit the list, but the ~1970 tied at 2 share one
+    # bin of the candidate histogram, which the select resolves by radix.
+    inp["q_idx"][2] = 0
+    inp["q_idx"][2, :, 0] = 1.0
+    inp["K_idx"][2] = 0
+    inp["K_idx"][2, :, 0] = rng.choice(np.array([0.0, 1.0, 2.0, 3.0], np.float16), size=N,
+                                       p=[0.5, 0.46, 0.03, 0.01])
+    say("[fused index] fallbacks: ties, two-valued scores, planted sample, 4-valued")
+    ids, ns = _gpu_ids(inp)
+    r_ids, r_ns = _oracle_ids(orc, inp)
+    assert_ids_equal(ids, ns, r_ids, r_ns)
+    assert np.all(np.isin(planted, r_ids[1, 0, :2048]))

@@ -285,6 +285,11 @@ struct SelWs {
     uint32_t* done;      // [BT] finished filter tiles
     uint32_t* cand;      // [BT][kCap][2] (key, cell)
     uint32_t* pivot;     // [BT][2] (key, cell index) of the k-th kept cell
+    // fused many-token path
+    uint32_t* thr;       // [BT] candidate bound (key)
+    uint32_t* gcount;    // [BT] candidates appended
+    uint32_t* samp;      // [BT][kSampleCells] sample keys
+    uint2* fcand;        // [BT][kCandCap] (fp32 score bits, cell)
 };
 
 __host__ __device__ __forceinline__ bool token_selects(int nvis, int k, int dense_max)
@@ -732,17 +737,19 @@ __device__ __forceinline__ uint32_t row_excl_scan(uint32_t v, uint32_t& total,
     return base + x - v;
 }
 
-// Selects the k largest of the row's keys, which thread t holds for cells
-// c0 = t*KPT .. c0+KPT-1 (0 for cells past the token's position), and writes
-// the kept cells in ascending order, -1 padding and the count.
-template <int KPT>
-__device__ __forceinline__ void select_row(const uint32_t (&key)[KPT], int c0, int k, int cap,
-                                           int32_t* __restrict__ out, int32_t* __restrict__ n_out,
-                                           uint32_t* hist, uint32_t* s_wave, uint32_t* s_pick)
+// The k-th largest of the keys the kRowThreads threads hold (KPT each; 0 for
+// an absent key, below every real key): returns it, and in r the number of
+// keys equal to it that rank within the k largest.  Radix digits of 11, 11
+// and 10 bits with LDS histograms.
+// `each(f)` calls f(key) for every key this thread holds.
+template <class Each>
+__device__ __forceinline__ uint32_t row_kth_largest_each(Each each, uint32_t k, uint32_t& r,
+                                                         uint32_t* hist, uint32_t* s_wave,
+                                                         uint32_t* s_pick)
 {
     const int tid = threadIdx.x;
-    // Radix select of the k-th largest key.
-    uint32_t prefix = 0, pmask = 0, r = (uint32_t)k;
+    uint32_t prefix = 0, pmask = 0;
+    r = k;
 #pragma unroll 1
     for (int d = 0; d < 3; ++d) {
         const int shift = (d == 0) ? 21 : (d == 1) ? 10 : 0;
@@ -750,10 +757,10 @@ __device__ __forceinline__ void select_row(const uint32_t (&key)[KPT], int c0, i
         for (int i = tid; i < nb; i += kRowThreads)
             hist[i] = 0u;
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if ((key[j] & pmask) == prefix)
-                atomicAdd(&hist[(key[j] >> shift) & (uint32_t)(nb - 1)], 1u);
+        each([&](uint32_t v) {
+            if ((v & pmask) == prefix)
+                atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
+        });
         __syncthreads();
         // Bin holding the r-th largest: thread t sums bins nb-1-2t and
         // nb-2-2t (nb / kRowThreads = 2 or 1 bins per thread).
@@ -782,6 +789,34 @@ __device__ __forceinline__ void select_row(const uint32_t (&key)[KPT], int c0, i
         pmask |= (uint32_t)(nb - 1) << shift;
         __syncthreads();
     }
+    return prefix;
+}
+
+template <int KPT>
+__device__ __forceinline__ uint32_t row_kth_largest(const uint32_t (&key)[KPT], uint32_t k,
+                                                    uint32_t& r, uint32_t* hist, uint32_t* s_wave,
+                                                    uint32_t* s_pick)
+{
+    return row_kth_largest_each(
+        [&](auto f) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+                f(key[j]);
+        },
+        k, r, hist, s_wave, s_pick);
+}
+
+// Selects the k largest of the row's keys, which thread t holds for cells
+// c0 = t*KPT .. c0+KPT-1 (0 for cells past the token's position), and writes
+// the kept cells in ascending order, -1 padding and the count.
+template <int KPT>
+__device__ __forceinline__ void select_row(const uint32_t (&key)[KPT], int c0, int k, int cap,
+                                           int32_t* __restrict__ out, int32_t* __restrict__ n_out,
+                                           uint32_t* hist, uint32_t* s_wave, uint32_t* s_pick)
+{
+    const int tid = threadIdx.x;
+    uint32_t r;
+    const uint32_t prefix = row_kth_largest<KPT>(key, (uint32_t)k, r, hist, s_wave, s_pick);
 
     // prefix is the k-th largest key; r keys equal to it are kept, lowest
     // cells first.
@@ -915,6 +950,709 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
     select_row<KPT>(key, c0, k, cap, out, n_sel + b, hist, s_wave, s_pick);
 }
 
+// ------------------------------------------ many tokens: fused select ---
+//
+// For many tokens (T > 16) against rows of up to kFusedMaxCells cells the
+// score matrix is never written.  Four kernels:
+//   k_idx_sample   scores a fixed sample of kSampleCells cells of the row
+//                  (evenly spread, each at a hashed offset inside its stride)
+//                  for every token and writes their keys (0 where the token
+//                  cannot see the cell);
+//   k_sel_thresh   per token, a lower bound for the k-th largest key: the
+//                  r-th largest sample key, r = mu + 4 sqrt(mu) + 4 with mu =
+//                  k * (visible samples) / (visible cells) the expected number
+//                  of samples among the k largest; resets the token's
+//                  candidate count;
+//   k_idx_collect  the whole score GEMM on the matrix cores, keeping only the
+//                  (score, cell) pairs at or above the bound: per-token lists
+//                  in LDS, flushed to the token's candidate list with one
+//                  atomic per (workgroup, token);
+//   k_sel_cand     per token, the exact top-k among the candidates (radix
+//                  select on the key, then on the cell index among equal
+//                  keys, so ties go to the lower index) and the kept ids in
+//                  ascending order through an LDS bitmap of the row.
+// Exactness: the candidates are every visible cell whose key is at or above
+// the bound.  When there are at least k of them the row's k-th largest key is
+// at or above the bound, so every cell that can be kept is a candidate and
+// the selection among the candidates is the selection of the row.  A token
+// with fewer than k candidates (bound too high) or more than kCandCap (list
+// overflow, e.g. massive exact ties) scores its whole row again, with the
+// same matrix instructions and operand layout and so the same fp32 scores,
+// into its key row of the workspace and runs the register select of
+// k_sel_row on it.
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kSampleCells = 2048;    // sampled cells per row
+constexpr int kCandCap = 8192;        // candidates kept per token
+constexpr int kCollectList = 64;      // LDS candidate slots per (workgroup, token)
+constexpr int kFusedMaxCells = 65536; // longest row of the fused path (bitmap, registers)
+constexpr int kFusedMinCells = 16384; // shorter rows write their keys instead
+
+// Reduction-index permutation of the matrix-core score kernels: at step st,
+// lane group g (lanes 16g .. 16g+15) supplies row elements
+// 64*(st/2) + 16*g + 8*(st%2) .. +7, in both operands, so over a step pair a
+// lane reads 32 contiguous bytes of its row.
+__device__ __forceinline__ int kperm(int st, int grp)
+{
+    return 64 * (st >> 1) + 16 * grp + 8 * (st & 1);
+}
+
+// Scores of 16 cells against 16 tokens on the matrix cores
+// (v_mfma_f32_16x16x32_f16): A = the cells' keys (lane l supplies row l%16),
+// B = the tokens' index queries (lane l supplies column l%16).  Lane l gets
+// cells 4*(l/16) + e, e = 0..3, of token column l%16.  Each element is the
+// same dot product in the same order whatever else shares the instruction.
+template <int KS>
+__device__ __forceinline__ float4_t score_block(const h8_t (&kc)[KS], const h8_t (&qt)[KS])
+{
+    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kc[st], qt[st], acc, 0, 0, 0);
+    return acc;
+}
+
+// Cell of sample s of a row whose sampled span is `span` cells (< span).
+__device__ __forceinline__ int sample_cell(int s, int span)
+{
+    const int stride = max(1, span / kSampleCells);
+    return s * stride + (int)((((uint32_t)s * 0x9E3779B1u) >> 16) % (uint32_t)stride);
+}
+
+// The smallest score whose key is `key` (inverse of score_key): a score s
+// satisfies score_key(s) >= key exactly when s >= key_to_score(key).  Key 0
+// (take every cell) gives -inf; key 0xffffffff (take none) gives NaN, which
+// no comparison passes.
+__device__ __forceinline__ float key_to_score(uint32_t key)
+{
+    if (key == 0u)
+        return -INFINITY;
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Grid (kSampleCells / 256, ceil(T / 64), B); a wave scores 64 tokens
+// against 64 samples, 16 samples per step.
+template <int DI>
+__global__ __launch_bounds__(256) void k_idx_sample(const _Float16* __restrict__ q_idx,
+                                                    const _Float16* __restrict__ K_idx,
+                                                    uint32_t* __restrict__ samp, int T, int N,
+                                                    int pos0, int span)
+{
+    constexpr int KS = DI / 32;
+    const int b = blockIdx.z;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int tok0 = blockIdx.y * 64;
+    const int s_base = (blockIdx.x * 4 + w) * 64;
+    h8_t qt[4][KS];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = min(tok0 + 16 * i + r, T - 1);
+        const _Float16* src = q_idx + ((size_t)b * T + tok) * DI;
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            qt[i][st] = *(const h8_t*)(src + kperm(st, grp));
+    }
+#pragma unroll 1
+    for (int g16 = 0; g16 < 4; ++g16) {
+        const int s0 = s_base + 16 * g16;
+        const int cell = sample_cell(s0 + r, span);
+        const _Float16* src = K_idx + ((size_t)b * N + cell) * DI;
+        h8_t kc[KS];
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            kc[st] = *(const h8_t*)(src + kperm(st, grp));
+        int ce[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            ce[e] = sample_cell(s0 + 4 * grp + e, span);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4_t acc = score_block<KS>(kc, qt[i]);
+            const int tok = tok0 + 16 * i + r;
+            if (tok < T) {
+                const int nvis = pos0 + tok + 1;
+                uint4 v;
+                v.x = ce[0] < nvis ? score_key(acc[0]) : 0u;
+                v.y = ce[1] < nvis ? score_key(acc[1]) : 0u;
+                v.z = ce[2] < nvis ? score_key(acc[2]) : 0u;
+                v.w = ce[3] < nvis ? score_key(acc[3]) : 0u;
+                *(uint4*)(samp + ((size_t)b * T + tok) * kSampleCells + s0 + 4 * grp) = v;
+            }
+        }
+    }
+}
+
+// ---- 256-thread k-th largest (sample bounds, candidate lists) ----------
+
+// Bitwise OR and AND over the workgroup (kSelThreads threads).
+__device__ __forceinline__ void wg_or_and(uint32_t& o, uint32_t& a, uint32_t* s_red)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        o |= (uint32_t)__shfl_xor((int)o, m, 64);
+        a &= (uint32_t)__shfl_xor((int)a, m, 64);
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        s_red[w] = o;
+        s_red[4 + w] = a;
+    }
+    __syncthreads();
+    o = s_red[0] | s_red[1] | s_red[2] | s_red[3];
+    a = s_red[4] & s_red[5] & s_red[6] & s_red[7];
+    __syncthreads();
+}
+
+// Minimum over the workgroup (kSelThreads threads); every thread gets it.
+__device__ __forceinline__ float wg_min_f(float v, uint32_t* s_red)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fminf(v, __shfl_xor(v, m, 64));
+    if ((threadIdx.x & 63) == 0)
+        s_red[threadIdx.x >> 6] = __float_as_uint(v);
+    __syncthreads();
+    v = fminf(fminf(__uint_as_float(s_red[0]), __uint_as_float(s_red[1])),
+              fminf(__uint_as_float(s_red[2]), __uint_as_float(s_red[3])));
+    __syncthreads();
+    return v;
+}
+
+// Bin of a descending walk over nb bins holding the r-th element, and the
+// number of elements in higher bins (every thread gets both).
+__device__ __forceinline__ void wg_find_bin(const uint32_t* hist, int nb, uint32_t r, uint32_t& bin,
+                                            uint32_t& above, uint32_t* s_wave, uint32_t* s_pick)
+{
+    // Thread t owns bins [nb - per (t + 1), nb - per t), read as vectors when
+    // per >= 4 (contiguous per thread: no bank conflicts), walked downwards.
+    const int per = (nb + kSelThreads - 1) / kSelThreads;
+    const int lo = nb - per * ((int)threadIdx.x + 1);
+    uint32_t c[8];
+    if (per == 8) {
+        const uint4 x = *(const uint4*)(hist + lo), y = *(const uint4*)(hist + lo + 4);
+        c[0] = x.x; c[1] = x.y; c[2] = x.z; c[3] = x.w;
+        c[4] = y.x; c[5] = y.y; c[6] = y.z; c[7] = y.w;
+    } else if (per == 4) {
+        const uint4 x = *(const uint4*)(hist + lo);
+        c[0] = x.x; c[1] = x.y; c[2] = x.z; c[3] = x.w;
+    } else {
+        for (int i = 0; i < per; ++i)
+            c[i] = (lo + i >= 0) ? hist[lo + i] : 0u;
+    }
+    uint32_t sum = 0;
+    for (int i = 0; i < per; ++i)
+        sum += c[i];
+    uint32_t total;
+    const uint32_t ex = block_excl_scan(sum, total, s_wave);
+    if (ex < r && r <= ex + sum) {
+        uint32_t acc = ex;
+        for (int i = per - 1; i >= 0; --i) {
+            if (acc < r && r <= acc + c[i]) {
+                s_pick[0] = (uint32_t)(lo + i);
+                s_pick[1] = acc;
+            }
+            acc += c[i];
+        }
+    }
+    __syncthreads();
+    bin = s_pick[0];
+    above = s_pick[1];
+    __syncthreads();
+}
+
+// The r-th largest (1-based, r at most their number) of the nonzero keys the
+// workgroup holds; `each(f)` calls f(key) for every key of this thread (0 =
+// no key, never counted).  On return r is the number of keys equal to the
+// result that rank within the r largest.  Radix digits of up to 11 bits,
+// starting below the bits that all keys share, so clustered keys (all above
+// a bound) spread over the bins.
+template <class Each>
+__device__ uint32_t wg_kth_largest(Each each, uint32_t& r, uint32_t* hist, uint32_t* s_red,
+                                   uint32_t* s_wave, uint32_t* s_pick)
+{
+    uint32_t o = 0u, a = 0xffffffffu;
+    each([&](uint32_t v) {
+        if (v) {
+            o |= v;
+            a &= v;
+        }
+    });
+    wg_or_and(o, a, s_red);
+    const uint32_t diff = o ^ a;
+    if (diff == 0u)
+        return a;   // one distinct key
+    int rem = 32 - __clz(diff);
+    uint32_t pmask = rem == 32 ? 0u : ~((1u << rem) - 1u);
+    uint32_t prefix = a & pmask;
+#pragma unroll 1
+    while (rem > 0) {
+        const int nbits = min(11, rem);
+        const int shift = rem - nbits;
+        const int nb = 1 << nbits;
+        for (int i = threadIdx.x; i < nb; i += kSelThreads)
+            hist[i] = 0u;
+        __syncthreads();
+        each([&](uint32_t v) {
+            if (v && (v & pmask) == prefix)
+                atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
+        });
+        __syncthreads();
+        uint32_t bin, above;
+        wg_find_bin(hist, nb, r, bin, above, s_wave, s_pick);
+        r -= above;
+        prefix |= bin << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        rem = shift;
+    }
+    return prefix;
+}
+
+// One workgroup per token: the candidate bound from the token's sample keys.
+__global__ __launch_bounds__(kSelThreads) void k_sel_thresh(const uint32_t* __restrict__ samp,
+                                                            uint32_t* __restrict__ thr,
+                                                            uint32_t* __restrict__ gcount, int T,
+                                                            int pos0, int k, int dense_max)
+{
+    constexpr int M = kSampleCells / kSelThreads;
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t s_wave[kSelThreads / 64];
+    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_red[8];
+    const int bt = blockIdx.x;
+    const int nvis = pos0 + bt % T + 1;
+    if (!token_selects(nvis, k, dense_max)) {
+        if (threadIdx.x == 0) {
+            thr[bt] = 0xffffffffu;   // above every score key: no candidates
+            gcount[bt] = 0u;
+        }
+        return;
+    }
+    const uint32_t* row = samp + (size_t)bt * kSampleCells;
+    uint32_t v[M];
+    uint32_t nv = 0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        v[m] = row[m * kSelThreads + threadIdx.x];
+        nv += v[m] != 0u ? 1u : 0u;
+    }
+    uint32_t total;
+    block_excl_scan(nv, total, s_wave);
+    const float mu = (float)k * (float)total / (float)nvis;
+    uint32_t r = (uint32_t)ceilf(mu + 4.f * sqrtf(mu) + 4.f);
+    uint32_t bound = 0u;   // 0: every visible cell is a candidate
+    if (r < total)
+        bound = wg_kth_largest(
+            [&](auto f) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    f(v[m]);
+            },
+            r, hist, s_red, s_wave, s_pick);
+    if (threadIdx.x == 0) {
+        thr[bt] = bound;
+        gcount[bt] = 0u;
+    }
+}
+
+// Grid: 8 x (cell ranges of 1024 per XCD) x ceil(T / 64) x B workgroups,
+// arranged so that the workgroups of one cell range run on one XCD one
+// after another (dispatch goes round-robin over the 8 XCDs): the range's
+// keys stay in that XCD's L2 for all its token blocks.  The four waves share
+// 64 tokens (four 16-token column blocks), whose query operands sit in LDS;
+// a wave walks 256 cells, 32 per step, with the next step's keys in flight,
+// and keeps the (score, cell) pairs at or above each token's bound.
+template <int DI>
+__global__ __launch_bounds__(256) void k_idx_collect(const _Float16* __restrict__ q_idx,
+                                                     const _Float16* __restrict__ K_idx,
+                                                     const uint32_t* __restrict__ thr,
+                                                     uint32_t* __restrict__ gcount,
+                                                     uint2* __restrict__ cand, int T, int N,
+                                                     int pos0, int n_cr, int n_tb, int B)
+{
+    constexpr int KS = DI / 32;
+    // Row pitch kCollectList + 1 entries, so the lists of the 16 tokens that
+    // one instruction appends to start on different LDS banks.
+    __shared__ uint2 lst[64][kCollectList + 1];
+    __shared__ uint32_t cnt[64];
+    // Query operands: slot (i, st) holds, for lane (r, g), token 16 i + r,
+    // elements kperm(st, g): one 16-byte slot per lane, lanes contiguous.
+    __shared__ h8_t qs[4][KS][64];
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int tb = local % n_tb;
+    const int crb = (local / n_tb) * 8 + xcd;     // (problem, cell range) index
+    if (crb >= n_cr * B)
+        return;
+    const int b = crb / n_cr, cr = crb % n_cr;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int tok0 = tb * 64;
+    const int cell_base = cr * 1024 + w * 256;
+    const int nvis_hi = pos0 + min(tok0 + 64, T);   // cells seen by the block's last token
+    const int nvis_lo = pos0 + tok0 + 1;             // cells seen by its first token
+    if (threadIdx.x < 64)
+        cnt[threadIdx.x] = 0u;
+    {   // wave w fills column block w of the query operands
+        const int tok = min(tok0 + 16 * w + r, T - 1);
+        const _Float16* src = q_idx + ((size_t)b * T + tok) * DI;
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            qs[w][st][lane] = *(const h8_t*)(src + kperm(st, grp));
+    }
+    float thf[4];   // score bound of the lane's token in each column block
+    int nv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = tok0 + 16 * i + r;
+        thf[i] = key_to_score(tok < T ? thr[(size_t)b * T + tok] : 0xffffffffu);
+        nv[i] = pos0 + tok + 1;
+    }
+    const int n_steps = max(0, min(8, (nvis_hi - cell_base + 31) / 32));
+    auto load_step = [&](int cb, h8_t (&kc)[2][KS]) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int cell = min(cell_base + 32 * cb + 16 * jj + r, nvis_hi - 1);
+            const _Float16* src = K_idx + ((size_t)b * N + cell) * DI;
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+                kc[jj][st] = *(const h8_t*)(src + kperm(st, grp));
+        }
+    };
+
+    // One step: the eight products (independent accumulators, so the matrix
+    // instructions pipeline), then the keys of step cb + 1 into the same
+    // registers, then the candidates while those are in flight.
+    auto step = [&](int cb, h8_t (&kc)[2][KS]) {
+        float4_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h8_t qv[KS];
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+                qv[st] = qs[i][st][lane];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                acc[i][jj] = score_block<KS>(kc[jj], qv);
+        }
+        if (cb + 1 < n_steps)
+            load_step(cb + 1, kc);
+        const int c0 = cell_base + 32 * cb;
+        // Candidate masks, bit 4*jj + e: cell c0 + 16 jj + 4 grp + e of the
+        // lane's token in column block i (non-short-circuit tests, no
+        // branches; visibility only where part of the step lies past a token).
+        uint32_t mk[4];
+        if (c0 + 32 <= nvis_lo) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mk[i] = 0u;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mk[i] |= (acc[i][jj][e] >= thf[i]) ? 1u << (4 * jj + e) : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mk[i] = 0u;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mk[i] |= ((acc[i][jj][e] >= thf[i]) & (c0 + 16 * jj + 4 * grp + e < nv[i]))
+                                     ? 1u << (4 * jj + e) : 0u;
+            }
+        }
+        // Appends the candidates of column block i (accumulators a0, a1 by
+        // value, so nothing is indexed at run time).
+        auto append = [&](int i, float4_t a0, float4_t a1, uint32_t mm) {
+            const int tl = 16 * i + r;
+            const uint32_t n = (uint32_t)__popc(mm);
+            uint32_t slot = atomicAdd(&cnt[tl], n);
+            // Each set bit in turn (a few per lane at most): the element is
+            // picked from the accumulators by its bit position.
+            while (mm) {
+                const uint32_t bp = (uint32_t)__builtin_ctz(mm);
+                mm &= mm - 1u;
+                const float4_t a4 = (bp & 4u) ? a1 : a0;
+                const float x0 = (bp & 2u) ? a4[2] : a4[0];
+                const float x1 = (bp & 2u) ? a4[3] : a4[1];
+                const uint2 ent = make_uint2(
+                    __float_as_uint((bp & 1u) ? x1 : x0),
+                    (uint32_t)(c0 + 16 * (int)(bp >> 2) + 4 * grp + (int)(bp & 3u)));
+                if (slot < (uint32_t)kCollectList) {
+                    lst[tl][slot] = ent;
+                } else {   // the token's LDS list is full: straight to its list
+                    const size_t bt = (size_t)b * T + tok0 + tl;
+                    const uint32_t p = atomicAdd(&gcount[bt], 1u);
+                    if (p < (uint32_t)kCandCap)
+                        cand[bt * kCandCap + p] = ent;
+                }
+                ++slot;
+            }
+        };
+        append(0, acc[0][0], acc[0][1], mk[0]);
+        append(1, acc[1][0], acc[1][1], mk[1]);
+        append(2, acc[2][0], acc[2][1], mk[2]);
+        append(3, acc[3][0], acc[3][1], mk[3]);
+    };
+
+    h8_t kc[2][KS];
+    if (n_steps > 0)
+        load_step(0, kc);
+    __syncthreads();   // query operands and list counts ready
+#pragma unroll 1
+    for (int cb = 0; cb < n_steps; ++cb)
+        step(cb, kc);
+    __syncthreads();
+    // Flush: wave w appends the lists of tokens 16w .. 16w+15, reserving all
+    // sixteen slot ranges at once (lane j for token 16w + j).
+    const int tl_l = 16 * w + (lane & 15);
+    const int tok_l = tok0 + tl_l;
+    const uint32_t n_l = (tok_l < T) ? min(cnt[tl_l], (uint32_t)kCollectList) : 0u;
+    uint32_t base_l = 0;
+    if (lane < 16 && n_l)
+        base_l = atomicAdd(&gcount[(size_t)b * T + tok_l], n_l);
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t n = (uint32_t)__shfl((int)n_l, j, 64);
+        if (n == 0)
+            continue;
+        const uint32_t base = (uint32_t)__shfl((int)base_l, j, 64);
+        const int tl = 16 * w + j;
+        uint2* dst = cand + ((size_t)b * T + tok0 + tl) * kCandCap;
+        for (uint32_t idx = lane; idx < n; idx += 64)
+            if (base + idx < (uint32_t)kCandCap)
+                dst[base + idx] = lst[tl][idx];
+    }
+}
+
+// One workgroup per token: the exact top-k among its candidates, or the
+// whole-row fallback (see above).
+template <int DI>
+__global__ __launch_bounds__(kSelThreads) void k_sel_cand(const _Float16* __restrict__ q_idx,
+                                                          const _Float16* __restrict__ K_idx,
+                                                          const uint32_t* __restrict__ gcount,
+                                                          const uint2* __restrict__ cand,
+                                                          uint32_t* __restrict__ keys,
+                                                          int32_t* __restrict__ ids,
+                                                          int32_t* __restrict__ n_sel, int T,
+                                                          int N, int pos0, int k, int dense_max,
+                                                          int cap)
+{
+    constexpr int CPT = kCandCap / kSelThreads;    // candidates per thread
+    constexpr int WPT = kFusedMaxCells / 32 / kSelThreads;   // bitmap words per thread
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t s_wave[kSelThreads / 64];
+    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_red[8];
+    __shared__ uint32_t bm[kFusedMaxCells / 32];
+    const int bt = blockIdx.x, tid = threadIdx.x;
+    const int nvis = pos0 + bt % T + 1;
+    int32_t* out = ids + (size_t)bt * cap;
+    if (!token_selects(nvis, k, dense_max)) {
+        if (tid == 0)
+            n_sel[bt] = nvis;
+        for (int i = tid; i < cap; i += kSelThreads)
+            out[i] = (i < nvis) ? i : -1;
+        return;
+    }
+    const uint32_t nc = gcount[bt];
+    if (nc >= (uint32_t)k && nc <= (uint32_t)kCandCap) {
+        const uint2* cr = cand + (size_t)bt * kCandCap;
+        float sc[CPT];      // scores (-inf: empty slot)
+        uint32_t cc[CPT];   // cells
+        float smax = -INFINITY, smin = INFINITY;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const uint32_t i = (uint32_t)(j * kSelThreads + tid);
+            const uint2 e = i < nc ? cr[i] : make_uint2(__float_as_uint(-INFINITY), 0u);
+            sc[j] = __uint_as_float(e.x);
+            cc[j] = e.y;
+            if (i < nc) {
+                smax = fmaxf(smax, sc[j]);
+                smin = fminf(smin, sc[j]);
+            }
+        }
+        // Linear bins over [smin, smax]: bin(s) = floor((s - smin) * nb / (smax - smin)),
+        // evaluated in fp32; every step is monotone, so bin order follows score order
+        // and equal scores share a bin.
+        smax = -wg_min_f(-smax, s_red);
+        smin = wg_min_f(smin, s_red);
+        float inv = (smax > smin) ? (float)kBins / (smax - smin) : 0.f;
+        if (!(inv < INFINITY))
+            inv = 0.f;   // range too narrow to scale: one bin, radix path below
+        auto bin_of = [&](float x) { return min(kBins - 1, (int)((x - smin) * inv)); };
+        for (int i = tid; i < kBins; i += kSelThreads)
+            hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+            if ((uint32_t)(j * kSelThreads + tid) < nc)
+                atomicAdd(&hist[bin_of(sc[j])], 1u);
+        __syncthreads();
+        uint32_t tb, above;   // bin of the k-th largest, count in higher bins
+        wg_find_bin(hist, kBins, (uint32_t)k, tb, above, s_wave, s_pick);
+        const uint32_t need = (uint32_t)k - above;   // kept from bin tb
+        // The members of bin tb, then each one's rank among them by (score desc,
+        // cell asc); the `need` best are kept.
+        if (tid == 0)
+            s_red[0] = 0u;
+        __syncthreads();
+        uint2* mem = (uint2*)bm;   // reused: at most kSelThreads members
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+            if ((uint32_t)(j * kSelThreads + tid) < nc && bin_of(sc[j]) == (int)tb) {
+                const uint32_t slot = atomicAdd(&s_red[0], 1u);
+                if (slot < (uint32_t)kSelThreads)
+                    mem[slot] = make_uint2(__float_as_uint(sc[j]), cc[j]);
+            }
+        __syncthreads();
+        const uint32_t m = s_red[0];
+        uint32_t keep_cell = 0xffffffffu;   // this thread's kept member of bin tb
+        if (m <= (uint32_t)kSelThreads) {
+            if (tid < (int)m) {
+                const float x = __uint_as_float(mem[tid].x);
+                const uint32_t c = mem[tid].y;
+                uint32_t rank = 0;
+                for (uint32_t i = 0; i < m; ++i) {
+                    const float y = __uint_as_float(mem[i].x);
+                    rank += (y > x || (y == x && mem[i].y < c)) ? 1u : 0u;
+                }
+                if (rank < need)
+                    keep_cell = c;
+            }
+        }
+        __syncthreads();
+        const int nw = (nvis + 31) >> 5;
+        for (int i = tid; i < nw; i += kSelThreads)
+            bm[i] = 0u;
+        __syncthreads();
+        if (m <= (uint32_t)kSelThreads) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+                if ((uint32_t)(j * kSelThreads + tid) < nc && bin_of(sc[j]) > (int)tb)
+                    atomicOr(&bm[cc[j] >> 5], 1u << (cc[j] & 31));
+            if (keep_cell != 0xffffffffu)
+                atomicOr(&bm[keep_cell >> 5], 1u << (keep_cell & 31));
+        } else {
+            // Heavy ties in one bin: exact radix select over all candidates,
+            // read again from the list (keys), then on the cell index among
+            // the keys equal to the k-th.
+            auto key_at = [&](uint32_t i) { return score_key(__uint_as_float(cr[i].x)); };
+            uint32_t req = (uint32_t)k;
+            const uint32_t tau = wg_kth_largest(
+                [&](auto f) {
+                    for (uint32_t i = tid; i < nc; i += kSelThreads)
+                        f(key_at(i));
+                },
+                req, hist, s_red, s_wave, s_pick);
+            uint32_t nties = 0;
+            for (uint32_t i = tid; i < nc; i += kSelThreads)
+                nties += key_at(i) == tau ? 1u : 0u;
+            uint32_t ties;
+            block_excl_scan(nties, ties, s_wave);
+            uint32_t cut = 0xffffffffu;
+            if (ties > req) {
+                uint32_t r2 = req;
+                cut = ~wg_kth_largest(
+                    [&](auto f) {
+                        for (uint32_t i = tid; i < nc; i += kSelThreads)
+                            f(key_at(i) == tau ? ~cr[i].y : 0u);
+                    },
+                    r2, hist, s_red, s_wave, s_pick);
+            }
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const uint32_t kj = (uint32_t)(j * kSelThreads + tid) < nc ? score_key(sc[j]) : 0u;
+                if (kj > tau || (kj == tau && kj != 0u && cc[j] <= cut))
+                    atomicOr(&bm[cc[j] >> 5], 1u << (cc[j] & 31));
+            }
+        }
+        __syncthreads();
+        uint32_t wd[WPT];
+        uint32_t cntw = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int wi = WPT * tid + i;
+            wd[i] = wi < nw ? bm[wi] : 0u;
+            cntw += (uint32_t)__popc(wd[i]);
+        }
+        uint32_t total;
+        uint32_t pos = block_excl_scan(cntw, total, s_wave);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i)
+            for (uint32_t mm = wd[i]; mm && pos < (uint32_t)k; mm &= mm - 1)
+                out[pos++] = 32 * (WPT * tid + i) + __builtin_ctz(mm);
+        for (int i = k + tid; i < cap; i += kSelThreads)
+            out[i] = -1;
+        if (tid == 0)
+            n_sel[bt] = k;
+        return;
+    }
+
+    // Fallback: the whole row again (as k_idx_collect computes it) into the
+    // token's key row, then the exact select over that row.
+    constexpr int KS = DI / 32;
+    const int lane = tid & 63, wv = tid >> 6, r = lane & 15, grp = lane >> 4;
+    const int b = bt / T;
+    h8_t qt[KS];   // the token's query in every column
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+        qt[st] = *(const h8_t*)(q_idx + (size_t)bt * DI + kperm(st, grp));
+    uint32_t* kr = keys + (size_t)bt * N;
+    for (int c0 = 16 * wv; c0 < nvis; c0 += 16 * (kSelThreads / 64)) {
+        const int cell = min(c0 + r, nvis - 1);
+        const _Float16* src = K_idx + ((size_t)b * N + cell) * DI;
+        h8_t kc[KS];
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            kc[st] = *(const h8_t*)(src + kperm(st, grp));
+        const float4_t acc = score_block<KS>(kc, qt);
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c0 + 4 * grp + e < nvis)
+                    kr[c0 + 4 * grp + e] = score_key(acc[e]);
+        }
+    }
+    __threadfence_block();
+    __syncthreads();
+    // Radix select over the row as it stands in memory, then each thread
+    // takes a contiguous run of cells: counts, prefix sums, ordered writes.
+    uint32_t req = (uint32_t)k;
+    const uint32_t tau = wg_kth_largest(
+        [&](auto f) {
+            for (int i = tid; i < nvis; i += kSelThreads)
+                f(kr[i]);
+        },
+        req, hist, s_red, s_wave, s_pick);
+    const int run = (nvis + kSelThreads - 1) / kSelThreads;
+    const int c0 = min(tid * run, nvis), c1 = min(c0 + run, nvis);
+    uint32_t gt = 0, eq = 0;
+    for (int c = c0; c < c1; ++c) {
+        const uint32_t u = kr[c];
+        gt += u > tau ? 1u : 0u;
+        eq += u == tau ? 1u : 0u;
+    }
+    uint32_t total;
+    const uint32_t eq_before = block_excl_scan(eq, total, s_wave);
+    const uint32_t take_eq = eq_before >= req ? 0u : min(eq, req - eq_before);
+    uint32_t pos = block_excl_scan(gt + take_eq, total, s_wave);
+    uint32_t taken = 0;
+    for (int c = c0; c < c1; ++c) {
+        const uint32_t u = kr[c];
+        const bool is_eq = u == tau;
+        if (u > tau || (is_eq && taken < take_eq))
+            out[pos++] = c;
+        taken += is_eq ? 1u : 0u;
+    }
+    for (int i = k + tid; i < cap; i += kSelThreads)
+        out[i] = -1;
+    if (tid == 0)
+        n_sel[bt] = k;
+}
+
 // Keys per thread of the single-block select for rows of N cells (0 if a row
 // is too long for it).
 static int row_select_kpt(int N)
@@ -928,6 +1666,7 @@ static int row_select_kpt(int N)
 // ------------------------------------------------------------- launch ---
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 
 static SelWs carve(void* ws, int B, int T, int N, size_t* total)
 {
@@ -949,6 +1688,12 @@ static SelWs carve(void* ws, int B, int T, int N, size_t* total)
     w.done = (uint32_t*)take(BT * 4);
     w.cand = (uint32_t*)take(BT * kCap * 8);
     w.pivot = (uint32_t*)take(BT * 8);
+    // fused many-token path (k_idx_sample .. k_sel_cand)
+    const bool fused = T > 16 && N <= kFusedMaxCells;
+    w.thr = (uint32_t*)take(fused ? BT * 4 : 0);
+    w.gcount = (uint32_t*)take(fused ? BT * 4 : 0);
+    w.samp = (uint32_t*)take(fused ? BT * kSampleCells * 4 : 0);
+    w.fcand = (uint2*)take(fused ? BT * kCandCap * 8 : 0);
     if (total)
         *total = off;
     return w;
@@ -1003,6 +1748,30 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
             if (kpt <= 4) QSA_FUSED(64, 4); else if (kpt <= 8) QSA_FUSED(64, 8); else QSA_FUSED(64, 16);
         } else {
             if (kpt <= 4) QSA_FUSED(128, 4); else if (kpt <= 8) QSA_FUSED(128, 8); else QSA_FUSED(128, 16);
+        }
+#undef QSA_FUSED
+        return hipGetLastError();
+    }
+    const bool fused = any_select && a.T > 16 && a.N <= kFusedMaxCells &&
+                       nvis_max >= kFusedMinCells && a.k <= kCandCap / 2;
+    if (fused) {
+        const dim3 gs(kSampleCells / 256, (a.T + 63) / 64, a.B);
+        const int n_cr = (nvis_max + 1023) / 1024, n_tb = (a.T + 63) / 64;
+        const int gc = ((n_cr * a.B + 7) / 8) * 8 * n_tb;
+        const _Float16* q = (const _Float16*)a.q_idx;
+        const _Float16* K = (const _Float16*)a.K_idx;
+#define QSA_FUSED(DI)                                                                          \
+    k_idx_sample<DI><<<gs, 256, 0, s>>>(q, K, w.samp, a.T, a.N, a.pos0, nvis_max);             \
+    k_sel_thresh<<<BT, kSelThreads, 0, s>>>(w.samp, w.thr, w.gcount, a.T, a.pos0, a.k,          \
+                                            a.dense_max);                                     \
+    k_idx_collect<DI><<<gc, 256, 0, s>>>(q, K, w.thr, w.gcount, w.fcand, a.T, a.N, a.pos0, n_cr, \
+                                         n_tb, a.B);                                          \
+    k_sel_cand<DI><<<BT, kSelThreads, 0, s>>>(q, K, w.gcount, w.fcand, w.keys, a.ids, a.n_sel,  \
+                                              a.T, a.N, a.pos0, a.k, a.dense_max, a.cap)
+        if (a.DI == 64) {
+            QSA_FUSED(64);
+        } else {
+            QSA_FUSED(128);
         }
 #undef QSA_FUSED
         return hipGetLastError();
