@@ -21,15 +21,19 @@
  *
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing, keeps no state between calls and never
- *     synchronises; every call only enqueues kernels on `stream` (a
- *     hipStream_t passed as void*, NULL = the default stream) and returns.
+ *     library allocates nothing and never synchronises; every call only
+ *     enqueues kernels on `stream` (a hipStream_t passed as void*, NULL =
+ *     the default stream) and returns.  Two calls keep device state of the
+ *     library between calls: qsa_index_topk_noalloc (its fixed workspace)
+ *     and qsa_decode_window (its grid barrier words); the others keep none.
  *   - Arguments are validated on the host before anything is enqueued.  An
  *     invalid call returns a negative qsa_status and enqueues nothing.  A
  *     kernel launch failure returns QSA_ERR_HIP.  There is no device-side
  *     error reporting: contents (ids out of range, NaN scores) are not
  *     checked.
- *   - Calls are thread-safe (no global mutable state).
+ *   - Calls are thread-safe on the host.  On the device, calls of
+ *     qsa_index_topk_noalloc, and calls of qsa_decode_window, must not
+ *     overlap on one GPU (see there).
  *   - B = `batch` independent problems are processed by one call; problem b
  *     reads and writes the b-th slice of every tensor.
  *   - fp16 means IEEE binary16.
@@ -304,6 +308,66 @@ typedef struct qsa_append_desc {
 QSA_API int qsa_kv_append(const qsa_append_desc* desc, const float* k_new, const float* v_new,
                           const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc,
                           void* K_idx, void* stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_decode_window -- one decode step of the whole path in ONE kernel
+ * launch: qsa_kv_append, then qsa_index_topk, qsa_attend and
+ * qsa_merge_gated, each phase reading what the one before wrote.
+ *
+ * The "opus r20 ..." page (section 4, timings) times the QSA step of a
+ * decode token as one dependent window of dispatches; with few problems the
+ * gaps between separate launches cost more than their work.  Here one
+ * cooperative launch (every workgroup resident at once) runs the phases,
+ * separated by grid-wide barriers, with the device code of the separate
+ * calls.  The results equal those of the four calls with the same
+ * descriptors bit for bit: new cache codes, scales and index keys; ids and
+ * n_sel; the output.  The index phase computes the fp32 scores as
+ * qsa_index_topk does for batch < 128 or n_cells > 16384 and keeps the same
+ * exact top-k of them; for batch >= 128 with n_cells <= 16384,
+ * qsa_index_topk scores in another summation order, so ids can differ from
+ * its ids, within the rounding bound stated there (never where every
+ * partial sum is exact in fp32).
+ *
+ * Arguments are those of the four calls: pdesc/k_new/v_new/kidx_new/cache
+ * as qsa_kv_append; idesc/q_idx/K_idx/ids/n_sel as qsa_index_topk; adesc/
+ * q/cache/ids/n_sel as qsa_attend; gate/out as qsa_merge_gated.  The three
+ * descriptors must describe the same step: T = 1 in each, equal batch and
+ * n_cells, pdesc->pos0 == idesc->pos0 (the new token's cell, which its own
+ * index query sees), equal Hkv and D, equal ids_cap, equal d_idx when
+ * kidx_new is given, and the same resolved cache strides (else
+ * QSA_ERR_INVALID_ARG).  The partials live in the workspace.  Ksc and Vsc
+ * must be 16-byte aligned here.
+ *
+ * Workspace: at least qsa_decode_window_workspace(idesc, adesc) bytes,
+ * 256-byte aligned, contents on entry irrelevant.  Its first 32-bit word is
+ * 0 after a normal call; it is nonzero if a barrier wait gave up (about a
+ * second per barrier; only possible if the grid could not run together,
+ * which the cooperative launch excludes) -- the outputs of that call are
+ * then invalid and later window calls in the process are unreliable.
+ *
+ * Concurrency: every call on one GPU uses the same two barrier words in
+ * the library's device memory (they return to their start state after each
+ * call, so calls ordered on one stream and HIP graph replays are fine).
+ * Window calls that overlap on one GPU are not supported: their barriers
+ * interfere, and the results are undefined (the bounded waits still end
+ * every call).
+ *
+ * Supported: q and out fp32 (q_dtype = out_dtype = QSA_F32), algo AUTO or
+ * MATRIX; (Hq/Hkv, D) in {(12, 256), (4, 64)}; d_idx in {64, 128}; P a
+ * multiple of 4 up to 64; pos0 < 16384 (one workgroup selects a row from
+ * registers; longer rows are faster through the separate calls); else
+ * QSA_ERR_UNSUPPORTED.  QSA_ERR_HIP if the
+ * device cannot launch the kernel cooperatively.
+ * --------------------------------------------------------------------- */
+QSA_API size_t qsa_decode_window_workspace(const qsa_index_desc* idesc,
+                                           const qsa_attn_desc* adesc);
+
+QSA_API int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc* idesc,
+                              const qsa_attn_desc* adesc, const float* k_new,
+                              const float* v_new, const float* kidx_new, int8_t* Kq, void* Ksc,
+                              int8_t* Vq, void* Vsc, void* K_idx, const void* q_idx,
+                              const void* q, const void* gate, int32_t* ids, int32_t* n_sel,
+                              void* out, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -211,3 +211,67 @@ def test_noalloc_index_host_checks():
     big = _idesc(T=2048, n_cells=65536, pos0=63488)
     assert L.qsa_index_topk_workspace(ctypes.byref(big)) > qsa.QSA_NOALLOC_WORKSPACE_BYTES
     assert L.qsa_index_topk_noalloc(ctypes.byref(big), 16, 16, 16, 16, None) == WORKSPACE
+
+
+def _window_call(pd, idsc, ad, ws=256, ws_bytes=1 << 30, kidx=16, gate=16):
+    # 16 stands for any 16-byte aligned device pointer; nothing is launched
+    # because every case below fails validation.
+    return qb.lib().qsa_decode_window(
+        None if pd is None else ctypes.byref(pd), None if idsc is None else ctypes.byref(idsc),
+        None if ad is None else ctypes.byref(ad), 16, 16, kidx, 16, 16, 16, 16, 16, 16, 16,
+        gate, 16, 16, 16, ws, ws_bytes, None)
+
+
+def _window_descs(**kw):
+    B, N, pos0 = kw.pop("batch", 2), kw.pop("n_cells", 8192), kw.pop("pos0", 8191)
+    pd = _pdesc(batch=B, n_cells=N, pos0=pos0, Hkv=2, D=256, d_idx=128)
+    idsc = _idesc(batch=B, n_cells=N, pos0=pos0)
+    ad = _adesc(batch=B, n_cells=N)
+    return pd, idsc, ad
+
+
+def test_window_workspace_size():
+    _, idsc, ad = _window_descs()
+    L = qb.lib()
+    need = L.qsa_decode_window_workspace(ctypes.byref(idsc), ctypes.byref(ad))
+    rows = 2 * 24 * 32
+    assert need >= 2 * 8192 * 4 + rows * (2 + 256) * 4
+    assert L.qsa_decode_window_workspace(ctypes.byref(_idesc(batch=0)), ctypes.byref(ad)) == 0
+    assert L.qsa_decode_window_workspace(ctypes.byref(idsc), ctypes.byref(_adesc(D=48))) == 0
+
+
+def test_window_host_checks():
+    """qsa_decode_window validates its three descriptors, their agreement and
+    the workspace on the host; every rejected call enqueues nothing."""
+    pd, idsc, ad = _window_descs()
+    assert _window_call(None, idsc, ad) == INVALID
+    assert _window_call(pd, None, ad) == INVALID
+    assert _window_call(pd, idsc, None) == INVALID
+    # descriptors that disagree
+    for bad in (dict(T=2, pos0=8190), dict(pos0=100), dict(batch=3), dict(D=64),
+                dict(Hkv=1), dict(n_cells=8000, pos0=7999)):
+        p2 = _pdesc(**{**dict(batch=2, n_cells=8192, pos0=8191, Hkv=2, D=256, d_idx=128),
+                       **bad})
+        assert _window_call(p2, idsc, ad) == INVALID, bad
+    assert _window_call(pd, _idesc(batch=2, n_cells=8192, pos0=8191, ids_cap=2100), ad) == INVALID
+    assert _window_call(pd, idsc, _adesc(batch=2, n_cells=8192, T=2)) == INVALID
+    assert _window_call(pd, idsc, _adesc(batch=2, n_cells=8192,
+                                         strides=dict(kq_cell_stride=1024))) == INVALID
+    # d_idx must agree only when a new index key is written
+    p64 = _pdesc(batch=2, n_cells=8192, pos0=8191, Hkv=2, D=256, d_idx=64)
+    assert _window_call(p64, idsc, ad) == INVALID
+    # shapes and dtypes without a window kernel
+    for kw in (dict(q_dtype=1), dict(out_dtype=1), dict(algo=2), dict(P=6), dict(P=2)):
+        assert _window_call(pd, idsc, _adesc(batch=2, n_cells=8192, **kw)) == UNSUPPORTED, kw
+    pl = _pdesc(batch=2, n_cells=20000, pos0=16384, Hkv=2, D=256, d_idx=128)
+    assert _window_call(pl, _idesc(batch=2, n_cells=20000, pos0=16384),
+                        _adesc(batch=2, n_cells=20000)) == UNSUPPORTED       # row too long
+    pd8 = _pdesc(batch=2, n_cells=8192, pos0=8191, Hkv=3, D=256, d_idx=128)
+    assert _window_call(pd8, idsc, _adesc(batch=2, n_cells=8192, Hkv=3)) == UNSUPPORTED
+    # workspace
+    need = qb.lib().qsa_decode_window_workspace(ctypes.byref(idsc), ctypes.byref(ad))
+    assert _window_call(pd, idsc, ad, ws=None) == WORKSPACE
+    assert _window_call(pd, idsc, ad, ws_bytes=need - 1) == WORKSPACE
+    assert _window_call(pd, idsc, ad, ws=16) == WORKSPACE             # not 256-byte aligned
+    # misaligned gate and output
+    assert _window_call(pd, idsc, ad, gate=8) == INVALID

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 
-SOURCES = ("qsa_api.hip", "qsa_index.hip", "qsa_attend.hip", "qsa_attend_mma.hip", "qsa_append.hip")
+SOURCES = ("qsa_api.hip", "qsa_index.hip", "qsa_attend.hip", "qsa_attend_mma.hip", "qsa_append.hip",
+           "qsa_window.hip")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 ARCH = "gfx950"

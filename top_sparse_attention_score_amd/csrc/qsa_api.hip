@@ -129,6 +129,92 @@ int check_attn(const qsa_attn_desc* d, qsa::AttnLaunch* L)
     return QSA_OK;
 }
 
+// Validates an index call's descriptor and pointers and fills `a` (all but
+// the workspace).
+int fill_index(const qsa_index_desc* desc, const void* q_idx, const void* K_idx, int32_t* ids,
+               int32_t* n_sel, qsa::IndexLaunch* a)
+{
+    const int st = check_index(desc);
+    if (st != QSA_OK)
+        return st;
+    if (!q_idx || !K_idx || !ids || !n_sel)
+        return QSA_ERR_INVALID_ARG;
+    if (!aligned(q_idx, 16) || !aligned(K_idx, 16) || !aligned(ids, 4) || !aligned(n_sel, 4))
+        return QSA_ERR_INVALID_ARG;
+    a->B = desc->batch;
+    a->T = desc->T;
+    a->N = desc->n_cells;
+    a->DI = desc->d_idx;
+    a->k = desc->k;
+    a->pos0 = desc->pos0;
+    a->dense_max = desc->dense_max;
+    a->cap = desc->ids_cap;
+    a->q_idx = q_idx;
+    a->K_idx = K_idx;
+    a->ids = ids;
+    a->n_sel = n_sel;
+    a->ws = nullptr;
+    return QSA_OK;
+}
+
+// Validates an append call's descriptor and pointers and fills `a`.
+int fill_append(const qsa_append_desc* d, const float* k_new, const float* v_new,
+                const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc, void* K_idx,
+                qsa::AppendLaunch* a)
+{
+    if (!d)
+        return QSA_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->T < 1 || d->n_cells < 1 || d->pos0 < 0 || d->Hkv < 1 ||
+        d->D < 32 || d->D % 32 || d->reserved != 0)
+        return QSA_ERR_INVALID_ARG;
+    if ((long long)d->pos0 + d->T > d->n_cells)
+        return QSA_ERR_INVALID_ARG;
+    if (d->D > 1024)
+        return QSA_ERR_UNSUPPORTED;
+    if (kidx_new && (d->d_idx < 4 || d->d_idx % 4))
+        return QSA_ERR_INVALID_ARG;
+    if ((long long)d->batch * d->T * d->Hkv * (d->D / 32) > (1LL << 30))
+        return QSA_ERR_UNSUPPORTED;
+    if (!k_new || !v_new || !Kq || !Ksc || !Vq || !Vsc || (kidx_new && !K_idx))
+        return QSA_ERR_INVALID_ARG;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || (kidx_new && !aligned(kidx_new, 16)) ||
+        !aligned(Kq, 16) || !aligned(Vq, 16) || !aligned(Ksc, 2) || !aligned(Vsc, 2) ||
+        (kidx_new && !aligned(K_idx, 8)))
+        return QSA_ERR_INVALID_ARG;
+    const long long row = (long long)d->Hkv * d->D;
+    const long long srow = (long long)d->Hkv * (d->D / 32) * 2;
+    a->kq_cs = d->kq_cell_stride ? d->kq_cell_stride : row;
+    a->vq_cs = d->vq_cell_stride ? d->vq_cell_stride : row;
+    a->ksc_cs = d->ksc_cell_stride ? d->ksc_cell_stride : srow;
+    a->vsc_cs = d->vsc_cell_stride ? d->vsc_cell_stride : srow;
+    a->kq_bs = d->kq_batch_stride ? d->kq_batch_stride : a->kq_cs * d->n_cells;
+    a->vq_bs = d->vq_batch_stride ? d->vq_batch_stride : a->vq_cs * d->n_cells;
+    a->ksc_bs = d->ksc_batch_stride ? d->ksc_batch_stride : a->ksc_cs * d->n_cells;
+    a->vsc_bs = d->vsc_batch_stride ? d->vsc_batch_stride : a->vsc_cs * d->n_cells;
+    if (a->kq_cs < 0 || a->vq_cs < 0 || a->ksc_cs < 0 || a->vsc_cs < 0 || a->kq_bs < 0 ||
+        a->vq_bs < 0 || a->ksc_bs < 0 || a->vsc_bs < 0)
+        return QSA_ERR_INVALID_ARG;
+    if (a->kq_cs % 16 || a->vq_cs % 16 || a->kq_bs % 16 || a->vq_bs % 16 || a->ksc_cs % 2 ||
+        a->vsc_cs % 2 || a->ksc_bs % 2 || a->vsc_bs % 2)
+        return QSA_ERR_INVALID_ARG;
+    a->B = d->batch;
+    a->T = d->T;
+    a->N = d->n_cells;
+    a->pos0 = d->pos0;
+    a->Hkv = d->Hkv;
+    a->D = d->D;
+    a->DI = d->d_idx;
+    a->k_new = k_new;
+    a->v_new = v_new;
+    a->kidx_new = kidx_new;
+    a->Kq = Kq;
+    a->Ksc = (uint16_t*)Ksc;
+    a->Vq = Vq;
+    a->Vsc = (uint16_t*)Vsc;
+    a->K_idx = (uint16_t*)K_idx;
+    return QSA_OK;
+}
+
 size_t partial_rows(const qsa_attn_desc* d)
 {
     return (size_t)d->batch * (size_t)d->T * (size_t)d->Hq * (size_t)d->P;
@@ -162,29 +248,13 @@ size_t qsa_index_topk_workspace(const qsa_index_desc* desc)
 int qsa_index_topk(const qsa_index_desc* desc, const void* q_idx, const void* K_idx,
                    int32_t* ids, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream)
 {
-    const int st = check_index(desc);
+    qsa::IndexLaunch a;
+    const int st = fill_index(desc, q_idx, K_idx, ids, n_sel, &a);
     if (st != QSA_OK)
         return st;
-    if (!q_idx || !K_idx || !ids || !n_sel)
-        return QSA_ERR_INVALID_ARG;
-    if (!aligned(q_idx, 16) || !aligned(K_idx, 16) || !aligned(ids, 4) || !aligned(n_sel, 4))
-        return QSA_ERR_INVALID_ARG;
     const size_t need = qsa::index_workspace_bytes(desc->batch, desc->T, desc->n_cells);
     if (!ws || ws_bytes < need || !aligned(ws, 16))
         return QSA_ERR_WORKSPACE;
-    qsa::IndexLaunch a;
-    a.B = desc->batch;
-    a.T = desc->T;
-    a.N = desc->n_cells;
-    a.DI = desc->d_idx;
-    a.k = desc->k;
-    a.pos0 = desc->pos0;
-    a.dense_max = desc->dense_max;
-    a.cap = desc->ids_cap;
-    a.q_idx = q_idx;
-    a.K_idx = K_idx;
-    a.ids = ids;
-    a.n_sel = n_sel;
     a.ws = ws;
     if (qsa::launch_index_topk(a, (hipStream_t)stream) != hipSuccess)
         return QSA_ERR_HIP;
@@ -282,58 +352,72 @@ int qsa_kv_append(const qsa_append_desc* d, const float* k_new, const float* v_n
                   const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc,
                   void* K_idx, void* stream)
 {
-    if (!d)
-        return QSA_ERR_INVALID_ARG;
-    if (d->batch < 1 || d->T < 1 || d->n_cells < 1 || d->pos0 < 0 || d->Hkv < 1 ||
-        d->D < 32 || d->D % 32 || d->reserved != 0)
-        return QSA_ERR_INVALID_ARG;
-    if ((long long)d->pos0 + d->T > d->n_cells)
-        return QSA_ERR_INVALID_ARG;
-    if (d->D > 1024)
-        return QSA_ERR_UNSUPPORTED;
-    if (kidx_new && (d->d_idx < 4 || d->d_idx % 4))
-        return QSA_ERR_INVALID_ARG;
-    if ((long long)d->batch * d->T * d->Hkv * (d->D / 32) > (1LL << 30))
-        return QSA_ERR_UNSUPPORTED;
-    if (!k_new || !v_new || !Kq || !Ksc || !Vq || !Vsc || (kidx_new && !K_idx))
-        return QSA_ERR_INVALID_ARG;
-    if (!aligned(k_new, 16) || !aligned(v_new, 16) || (kidx_new && !aligned(kidx_new, 16)) ||
-        !aligned(Kq, 16) || !aligned(Vq, 16) || !aligned(Ksc, 2) || !aligned(Vsc, 2) ||
-        (kidx_new && !aligned(K_idx, 8)))
-        return QSA_ERR_INVALID_ARG;
     qsa::AppendLaunch a;
-    const long long row = (long long)d->Hkv * d->D;
-    const long long srow = (long long)d->Hkv * (d->D / 32) * 2;
-    a.kq_cs = d->kq_cell_stride ? d->kq_cell_stride : row;
-    a.vq_cs = d->vq_cell_stride ? d->vq_cell_stride : row;
-    a.ksc_cs = d->ksc_cell_stride ? d->ksc_cell_stride : srow;
-    a.vsc_cs = d->vsc_cell_stride ? d->vsc_cell_stride : srow;
-    a.kq_bs = d->kq_batch_stride ? d->kq_batch_stride : a.kq_cs * d->n_cells;
-    a.vq_bs = d->vq_batch_stride ? d->vq_batch_stride : a.vq_cs * d->n_cells;
-    a.ksc_bs = d->ksc_batch_stride ? d->ksc_batch_stride : a.ksc_cs * d->n_cells;
-    a.vsc_bs = d->vsc_batch_stride ? d->vsc_batch_stride : a.vsc_cs * d->n_cells;
-    if (a.kq_cs < 0 || a.vq_cs < 0 || a.ksc_cs < 0 || a.vsc_cs < 0 || a.kq_bs < 0 ||
-        a.vq_bs < 0 || a.ksc_bs < 0 || a.vsc_bs < 0)
-        return QSA_ERR_INVALID_ARG;
-    if (a.kq_cs % 16 || a.vq_cs % 16 || a.kq_bs % 16 || a.vq_bs % 16 || a.ksc_cs % 2 ||
-        a.vsc_cs % 2 || a.ksc_bs % 2 || a.vsc_bs % 2)
-        return QSA_ERR_INVALID_ARG;
-    a.B = d->batch;
-    a.T = d->T;
-    a.N = d->n_cells;
-    a.pos0 = d->pos0;
-    a.Hkv = d->Hkv;
-    a.D = d->D;
-    a.DI = d->d_idx;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.kidx_new = kidx_new;
-    a.Kq = Kq;
-    a.Ksc = (uint16_t*)Ksc;
-    a.Vq = Vq;
-    a.Vsc = (uint16_t*)Vsc;
-    a.K_idx = (uint16_t*)K_idx;
+    const int st = fill_append(d, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, &a);
+    if (st != QSA_OK)
+        return st;
     if (qsa::launch_kv_append(a, (hipStream_t)stream) != hipSuccess)
+        return QSA_ERR_HIP;
+    return QSA_OK;
+}
+
+size_t qsa_decode_window_workspace(const qsa_index_desc* idesc, const qsa_attn_desc* adesc)
+{
+    qsa::AttnLaunch at;
+    if (check_index(idesc) != QSA_OK || check_attn(adesc, &at) != QSA_OK)
+        return 0;
+    return qsa::window_workspace_bytes(idesc->batch, idesc->n_cells, adesc->Hq, adesc->P,
+                                       adesc->D);
+}
+
+int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc* idesc,
+                      const qsa_attn_desc* adesc, const float* k_new, const float* v_new,
+                      const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc,
+                      void* K_idx, const void* q_idx, const void* q, const void* gate,
+                      int32_t* ids, int32_t* n_sel, void* out, void* ws, size_t ws_bytes,
+                      void* stream)
+{
+    qsa::AppendLaunch ap;
+    qsa::IndexLaunch ix;
+    qsa::AttnLaunch at;
+    int st = fill_append(pdesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, &ap);
+    if (st == QSA_OK)
+        st = fill_index(idesc, q_idx, K_idx, ids, n_sel, &ix);
+    if (st == QSA_OK)
+        st = check_attn(adesc, &at);
+    if (st != QSA_OK)
+        return st;
+    // One step of the same problems, read from the cache the append writes.
+    if (pdesc->T != 1 || idesc->T != 1 || adesc->T != 1 || pdesc->batch != idesc->batch ||
+        adesc->batch != idesc->batch || pdesc->n_cells != idesc->n_cells ||
+        adesc->n_cells != idesc->n_cells || pdesc->pos0 != idesc->pos0 ||
+        pdesc->Hkv != adesc->Hkv || pdesc->D != adesc->D || adesc->ids_cap != idesc->ids_cap ||
+        (kidx_new && pdesc->d_idx != idesc->d_idx))
+        return QSA_ERR_INVALID_ARG;
+    if (ap.kq_cs != at.kq_cs || ap.ksc_cs != at.ksc_cs || ap.vq_cs != at.vq_cs ||
+        ap.vsc_cs != at.vsc_cs || ap.kq_bs != at.kq_bs || ap.ksc_bs != at.ksc_bs ||
+        ap.vq_bs != at.vq_bs || ap.vsc_bs != at.vsc_bs)
+        return QSA_ERR_INVALID_ARG;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16) || (gate && !aligned(gate, 16)) ||
+        !aligned(Ksc, 16) || !aligned(Vsc, 16))
+        return QSA_ERR_INVALID_ARG;
+    if (at.q_f16 || at.out_f16 || at.algo == QSA_ATTEND_VECTOR ||
+        !qsa::window_supported(at.Hq / at.Hkv, at.D, ix.DI, at.P, ix.pos0 + 1))
+        return QSA_ERR_UNSUPPORTED;
+    const size_t need =
+        qsa::window_workspace_bytes(idesc->batch, idesc->n_cells, adesc->Hq, adesc->P, adesc->D);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return QSA_ERR_WORKSPACE;
+    at.q = q;
+    at.Kq = Kq;
+    at.Ksc = Ksc;
+    at.Vq = Vq;
+    at.Vsc = Vsc;
+    at.ids = ids;
+    at.n_sel = n_sel;
+    at.out = out;
+    at.gate = gate;
+    if (qsa::launch_window(ap, ix, at, ws, (hipStream_t)stream) != hipSuccess)
         return QSA_ERR_HIP;
     return QSA_OK;
 }

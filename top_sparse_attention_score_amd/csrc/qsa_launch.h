@@ -71,4 +71,14 @@ hipError_t launch_attend(const AttnLaunch& a, hipStream_t s);
 bool launch_attend_mma(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_merge(const AttnLaunch& a, hipStream_t s);
 
+// Single-launch decode window (qsa_window.hip): append, index, attend and
+// gated merge of one token per problem in one cooperative kernel.
+bool window_supported(int G, int D, int DI, int P, int nvis);
+// Workspace: status word, [B][N] score keys, partials.
+size_t window_workspace_bytes(int B, int N, int Hq, int P, int D);
+// `ap`, `ix`, `at` describe the same T = 1 problems (the caller checks that);
+// the partial pointers of `at` are ignored (the window keeps them in `ws`).
+hipError_t launch_window(const AppendLaunch& ap, const IndexLaunch& ix, const AttnLaunch& at,
+                         void* ws, hipStream_t s);
+
 }  // namespace qsa

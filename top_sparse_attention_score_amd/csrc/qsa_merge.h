@@ -1,0 +1,123 @@
+// qsa_merge.h -- the log-sum-exp merge of split-KV partials as a device
+// function of one (virtual) workgroup, shared by the merge kernel and the
+// single-launch decode window ("opus r20 track A: MTP map mlock + qsa_attn /
+// qsa_merge decode tweaks", section 2 "qsa.metal", qsa_merge: rescale each
+// chunk by exp(m_c - M), fma in chunk order, then one division).
+#pragma once
+
+#include <math.h>
+
+#include "qsa_device.h"
+
+namespace qsa {
+
+constexpr int kMergeWaves = 4;
+
+// EPL (4 or 1) consecutive output elements per lane, D/EPL lanes per (token,
+// query head) row; a wave covers 64/(D/EPL) rows (EPL = 1 spreads rows with
+// many chunks over more waves).  Per element: M = max_c m_c, then over the
+// chunks in order e = exp(m_c - M) (0 for an empty chunk), L = fma(l_c, e,
+// L), y = fma(o_c, e, y), and one division.  An empty chunk has l = o = 0,
+// so its zero weight leaves L and y bitwise unchanged.  With a gate (same
+// layout and dtype as q), the result is multiplied by 1 / (1 + exp(-g)).
+template <int D, int EPL, bool OUTF16>
+__device__ __forceinline__ void merge_block(int blk, const float* __restrict__ pm,
+                                            const float* __restrict__ pl,
+                                            const float* __restrict__ po,
+                                            void* __restrict__ out, int P, long long rows,
+                                            const void* __restrict__ gate, int gate_f16)
+{
+    constexpr int LPR = D / EPL;   // lanes per row
+    constexpr int RPW = 64 / LPR;  // rows per wave (D = 64, EPL = 1: one row per wave)
+    static_assert(LPR <= 64 || LPR % 64 == 0, "rows map to whole lane groups or waves");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    long long r;
+    int de;  // first element of this lane
+    if constexpr (LPR <= 64) {
+        r = ((long long)blk * kMergeWaves + wave) * RPW + lane / LPR;
+        de = EPL * (lane % LPR);
+    } else {
+        constexpr int WPR = LPR / 64;  // waves per row
+        r = ((long long)blk * kMergeWaves + wave) / WPR;
+        de = EPL * (64 * (wave % WPR) + lane);
+    }
+    if (r >= rows)
+        return;
+    const float* m = pm + r * P;
+    const float* l = pl + r * P;
+    const float* o = po + r * P * D + de;
+    float M = -INFINITY;
+    for (int c = 0; c < P; ++c)
+        M = fmaxf(M, m[c]);
+    float L = 0.f;
+    float y[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        y[e] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+        for (int c = 0; c < P; ++c) {
+            const float mc = m[c];
+            const float w = (mc == -INFINITY) ? 0.f : expf(mc - M);
+            L = fmaf(l[c], w, L);
+            if constexpr (EPL == 4) {
+                const float4 v = *(const float4*)(o + (size_t)c * D);
+                y[0] = fmaf(v.x, w, y[0]);
+                y[1] = fmaf(v.y, w, y[1]);
+                y[2] = fmaf(v.z, w, y[2]);
+                y[3] = fmaf(v.w, w, y[3]);
+            } else {
+                y[0] = fmaf(o[(size_t)c * D], w, y[0]);
+            }
+        }
+    }
+    float res[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        res[e] = (L > 0.f) ? y[e] / L : 0.f;
+    if (gate) {
+        // output gate: res * sigmoid(g), elementwise
+        float gv[EPL];
+        if (gate_f16) {
+            const _Float16* gp = (const _Float16*)gate + r * D + de;
+            if constexpr (EPL == 4) {
+                const half4_t g4 = *(const half4_t*)gp;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gv[e] = (float)g4[e];
+            } else {
+                gv[0] = (float)gp[0];
+            }
+        } else {
+            const float* gp = (const float*)gate + r * D + de;
+            if constexpr (EPL == 4) {
+                const float4 g4 = *(const float4*)gp;
+                gv[0] = g4.x;
+                gv[1] = g4.y;
+                gv[2] = g4.z;
+                gv[3] = g4.w;
+            } else {
+                gv[0] = gp[0];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            res[e] *= 1.f / (1.f + expf(-gv[e]));
+    }
+    if constexpr (OUTF16) {
+        _Float16* dst = (_Float16*)out + r * D + de;
+        if constexpr (EPL == 4)
+            *(half4_t*)dst = half4_t{(_Float16)res[0], (_Float16)res[1], (_Float16)res[2],
+                                     (_Float16)res[3]};
+        else
+            dst[0] = (_Float16)res[0];
+    } else {
+        float* dst = (float*)out + r * D + de;
+        if constexpr (EPL == 4)
+            *(float4*)dst = make_float4(res[0], res[1], res[2], res[3]);
+        else
+            dst[0] = res[0];
+    }
+}
+
+}  // namespace qsa

@@ -90,6 +90,13 @@ def lib() -> ctypes.CDLL:
         L.qsa_kv_append.argtypes = [ctypes.POINTER(AppendDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp]
         L.qsa_kv_append.restype = _c_int
+        L.qsa_decode_window_workspace.argtypes = [ctypes.POINTER(IndexDesc),
+                                                  ctypes.POINTER(AttnDesc)]
+        L.qsa_decode_window_workspace.restype = ctypes.c_size_t
+        L.qsa_decode_window.argtypes = [ctypes.POINTER(AppendDesc), ctypes.POINTER(IndexDesc),
+                                        ctypes.POINTER(AttnDesc)] + [_vp] * 15 + \
+                                       [ctypes.c_size_t, _vp]
+        L.qsa_decode_window.restype = _c_int
         _lib = L
     return _lib
 
@@ -188,6 +195,21 @@ def qsa_kv_append(desc: AppendDesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_
     _check(lib().qsa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(kidx_new),
                                _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc), _ptr(K_idx),
                                _stream(stream)), "qsa_kv_append")
+
+
+def qsa_decode_window_workspace(idesc: IndexDesc, adesc: AttnDesc) -> int:
+    return int(lib().qsa_decode_window_workspace(ctypes.byref(idesc), ctypes.byref(adesc)))
+
+
+def qsa_decode_window(pdesc: AppendDesc, idesc: IndexDesc, adesc: AttnDesc, k_new, v_new,
+                      kidx_new, Kq, Ksc, Vq, Vsc, K_idx, q_idx, q, gate, ids, n_sel, out, ws,
+                      stream=None) -> None:
+    _check(lib().qsa_decode_window(
+        ctypes.byref(pdesc), ctypes.byref(idesc), ctypes.byref(adesc), _ptr(k_new), _ptr(v_new),
+        _ptr(kidx_new), _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc), _ptr(K_idx), _ptr(q_idx),
+        _ptr(q), _ptr(gate), _ptr(ids), _ptr(n_sel), _ptr(out), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+        "qsa_decode_window")
 
 
 # ------------------------------------------------------- whole-path plan ---
