@@ -81,34 +81,150 @@ def attend_flops(p: dict, n_sel_total: int) -> float:
 ATTEND_SOURCES = {"matrix": "qsa_attend_mma.hip", "vector": "qsa_attend.hip"}
 ATTEND_KERNELS = {"matrix": "k_attend_mma", "vector": "k_attend"}
 # Headers whose code the attend kernels compile in (also hashed).
-ATTEND_HEADERS = ("qsa_device.h", "qsa_mma.h")
+ATTEND_HEADERS = ("qsa_device.h", "qsa_mma.h", "qsa_attend_mma.h", "qsa_merge.h")
+# Source and headers of the index kernels (their hash gates profiled index
+# traffic).
+INDEX_FILES = ("qsa_index.hip", "qsa_select.h", "qsa_device.h", "qsa_mma.h")
 
 
-def profiled_traffic(workload: str, B: int, P: int, algo: str):
-    """HBM bytes per attend dispatch from the committed rocprofv3 summary of
-    this exact launch configuration (profiles/<kernel>_<workload>_b<B>_P<P>.md),
-    scaled by the copy-kernel calibration recorded there; None if there is no
-    such summary or the kernel source (with the device headers it includes)
-    changed since it was taken."""
+def source_hash(files) -> str:
     import hashlib
+    csrc = os.path.join(ROOT, "top_sparse_attention_score_amd", "csrc")
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                   for f in files)).hexdigest()[:16]
+
+
+def _profile_fields(workload: str, B: int, P: int, algo: str, layout: str) -> dict:
     kern = ATTEND_KERNELS[algo]
-    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_b{B}_P{P}.md")
-    src = os.path.join(ROOT, "top_sparse_attention_score_amd", "csrc", ATTEND_SOURCES[algo])
-    if not os.path.exists(path):
-        return None
+    tag = "" if layout == "dense" else f"_{layout}"
+    path = os.path.join(ROOT, "profiles", f"{kern}_{workload}_b{B}_P{P}{tag}.md")
     fields = {}
-    for line in open(path):
-        if ":" in line and not line.startswith(("|", "#", "`")):
-            key, _, val = line.partition(":")
-            fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in [src] + [
-        os.path.join(os.path.dirname(src), h) for h in ATTEND_HEADERS])).hexdigest()[:16]
-    if fields.get("traffic_source_sha256_16") != sha:
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and not line.startswith(("|", "#", "`")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    return fields
+
+
+def profiled_index_traffic(workload: str, B: int, P: int, algo: str, layout: str):
+    """HBM bytes of one index_topk call (all its kernels) from the same
+    committed summary; None if absent or the index sources changed."""
+    f = _profile_fields(workload, B, P, algo, layout)
+    if f.get("index_source_sha256_16") != source_hash(INDEX_FILES):
         return None
     try:
-        return int(fields["read_bytes_per_dispatch"]) + int(fields["write_bytes_per_dispatch"])
+        return int(f["index_read_bytes_per_call"]) + int(f["index_write_bytes_per_call"])
     except (KeyError, ValueError):
         return None
+
+
+def profiled_traffic(workload: str, B: int, P: int, algo: str, layout: str = "dense"):
+    """HBM bytes per attend dispatch from the committed rocprofv3 summary of
+    this exact launch configuration
+    (profiles/<kernel>_<workload>_b<B>_P<P>[_<layout>].md), scaled by the
+    copy-kernel calibration recorded there; None if there is no such summary
+    or the kernel source (with the device headers it includes) changed since
+    it was taken."""
+    f = _profile_fields(workload, B, P, algo, layout)
+    if f.get("traffic_source_sha256_16") != source_hash((ATTEND_SOURCES[algo],) +
+                                                        ATTEND_HEADERS):
+        return None
+    try:
+        return int(f["read_bytes_per_dispatch"]) + int(f["write_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def interleave_cache(dev: dict, B: int, N: int, Hkv: int, D: int):
+    """The cache as one row per cell: every head's K codes, then V codes,
+    then K scales, then V scales (Hkv*(2D + D/8) bytes); returns device views
+    at the four bases and the attention/append strides (bytes) that address
+    them.  The four regions of a cell are disjoint, so the append writes and
+    the attention reads the same cells as with the dense arrays."""
+    import torch
+    codes, sc = Hkv * D, Hkv * (D // 32) * 2
+    row = 2 * codes + 2 * sc
+    buf = torch.empty((B, N, row), dtype=torch.int8, device="cuda")
+    buf[:, :, :codes].copy_(dev["Kq"].reshape(B, N, codes))
+    buf[:, :, codes:2 * codes].copy_(dev["Vq"].reshape(B, N, codes))
+    buf[:, :, 2 * codes:2 * codes + sc].copy_(dev["Ksc"].reshape(B, N, -1).view(torch.int8))
+    buf[:, :, 2 * codes + sc:].copy_(dev["Vsc"].reshape(B, N, -1).view(torch.int8))
+    out = dict(dev)
+    out["Kq"] = buf[:, :, :codes]
+    out["Vq"] = buf[:, :, codes:2 * codes]
+    out["Ksc"] = buf[:, :, 2 * codes:2 * codes + sc]
+    out["Vsc"] = buf[:, :, 2 * codes + sc:]
+    out["kv_buffer"] = buf
+    strides = {f"{n}_cell_stride": row for n in ("kq", "ksc", "vq", "vsc")}
+    strides.update({f"{n}_batch_stride": row * N for n in ("kq", "ksc", "vq", "vsc")})
+    return out, strides
+
+
+def hbm_ceiling(inp: dict, dev: dict, path, B: int, P: int, attend_bytes: int,
+                attend_ms: float) -> dict:
+    """Attainable read rates measured by libhbm_probe.so on this GPU: one
+    streaming read of 2 GiB, and (one-token workloads) the attention's cell
+    gather alone -- the same kept ids, cache layout and split, no arithmetic.
+    Rates are GB/s of bytes the kernels must read; the attention stage's own
+    rate on its gathered bytes is given beside them."""
+    import ctypes
+
+    import torch
+
+    from top_sparse_attention_score_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: run __graft_entry__.build()")
+    L = ctypes.CDLL(PROBE_LIB)
+    vp, ll, ci = ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int
+    L.hbm_probe_stream.argtypes = [vp, ll, vp, ci, vp]
+    L.hbm_probe_gather_sink_words.argtypes = [ci, ci, ci]
+    L.hbm_probe_gather_sink_words.restype = ll
+    L.hbm_probe_gather.argtypes = [vp] * 4 + [ll] * 8 + [vp] + [ci] * 5 + [vp, vp]
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            rc = fn()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    n = 2 << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    grid = 4096
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    t = timed(lambda: L.hbm_probe_stream(buf.data_ptr(), n, sink.data_ptr(), grid,
+                                         stream.cuda_stream))
+    del buf
+    res = {"stream_read_gbs": round(n / t / 1e9, 1), "stream_bytes": n}
+    if inp["T"] == 1 and int(path.n_sel.min().item()) == int(path.n_sel.max().item()):
+        k = int(path.n_sel[0, 0].item())
+        ids = path.ids[:, 0, :k].contiguous()
+        a = path.adesc
+        Hkv, D = inp["Hkv"], inp["D"]
+        row, srow = Hkv * D, Hkv * (D // 32) * 2
+        cs = [a.kq_cell_stride or row, a.vq_cell_stride or row, a.ksc_cell_stride or srow,
+              a.vsc_cell_stride or srow]
+        bs = [a.kq_batch_stride or cs[0] * inp["N"], a.vq_batch_stride or cs[1] * inp["N"],
+              a.ksc_batch_stride or cs[2] * inp["N"], a.vsc_batch_stride or cs[3] * inp["N"]]
+        gsink = torch.zeros(L.hbm_probe_gather_sink_words(B, Hkv, P), dtype=torch.int32,
+                            device="cuda")
+        t = timed(lambda: L.hbm_probe_gather(
+            dev["Kq"].data_ptr(), dev["Vq"].data_ptr(), dev["Ksc"].data_ptr(),
+            dev["Vsc"].data_ptr(), *cs, *bs, ids.data_ptr(), B, k, Hkv, D, P,
+            gsink.data_ptr(), stream.cuda_stream))
+        gathered = B * k * Hkv * (2 * D + D // 8)
+        res.update(gather_gbs=round(gathered / t / 1e9, 1), gather_bytes=gathered,
+                   gather_us=round(t * 1e6, 1),
+                   attend_gather_gbs=round(gathered / (attend_ms * 1e-3) / 1e9, 1))
+    return res
 
 
 def host_record() -> dict:
@@ -183,7 +299,9 @@ def cpu_baseline(inp_cfg: str, target_s: float, P: int) -> dict:
 def single_problem_latency(qsa, base: dict, P: int, algo_code: int, steps: int = 50) -> dict:
     """One problem (B = 1) per step, the latency-bound case: the same step
     (append -> index_topk -> attend -> gated merge) launched eagerly, and
-    captured once in a HIP graph and replayed; microseconds per step."""
+    captured once in a HIP graph and replayed; then the step as the single
+    cooperative launch of qsa_decode_window (eagerly and from a graph);
+    microseconds per step."""
     import torch
     inp = {k: (v[:1] if hasattr(v, "shape") and getattr(v, "ndim", 0) and k in
                ("q_idx", "K_idx", "q", "Kq", "Ksc", "Vq", "Vsc") else v)
@@ -219,17 +337,36 @@ def single_problem_latency(qsa, base: dict, P: int, algo_code: int, steps: int =
         torch.cuda.synchronize()
         return round(e0.elapsed_time(e1) / steps * 1e3, 2)
 
-    eager = timed(step)
-    g = torch.cuda.CUDAGraph()
-    step()
-    torch.cuda.synchronize()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            step(side)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    return dict(eager=eager, graph=timed(g.replay))
+    def graph_of(fn):
+        g = torch.cuda.CUDAGraph()
+        fn()
+        torch.cuda.synchronize()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                fn(side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        return g
+
+    res = dict(eager=timed(step), graph=timed(graph_of(step).replay))
+    # The same step as one cooperative launch (qsa_decode_window), where the
+    # library has a window kernel for the shape.
+    ws_bytes = qsa.qsa_decode_window_workspace(path.idesc, path.adesc)
+    if ws_bytes and T == 1 and not inp["q_dtype"] == "f16" and inp["pos0"] < 16384:
+        ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.int32, device="cuda")
+        ids = torch.empty_like(path.ids)
+        n_sel = torch.empty_like(path.n_sel)
+        out = torch.empty_like(path.out)
+
+        def window(stream=None):
+            qsa.qsa_decode_window(adesc, path.idesc, path.adesc, k_new, v_new, i_new, dev["Kq"],
+                                  dev["Ksc"], dev["Vq"], dev["Vsc"], dev["K_idx"],
+                                  dev["q_idx"], dev["q"], dev["gate"], ids, n_sel, out, ws,
+                                  stream=stream)
+        res["window_eager"] = timed(window)
+        res["window_graph"] = timed(graph_of(window).replay)
+    return res
 
 
 def main() -> None:
@@ -248,6 +385,12 @@ def main() -> None:
                     help="skip the single-problem (B = 1) latency measurement")
     ap.add_argument("--algo", default="matrix", choices=["matrix", "vector"],
                     help="qsa_attend kernel family")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the attainable-HBM-rate probes")
+    ap.add_argument("--layout", default="interleaved", choices=["dense", "interleaved"],
+                    help="KV cache layout: dense arrays [B][N][Hkv][D] and [B][N][Hkv][D/32], "
+                         "or one row per cell holding every head's K codes, V codes, K "
+                         "scales and V scales (strided views of one buffer)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB "
                          "(a known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -277,8 +420,11 @@ def main() -> None:
         dev[key] = t.repeat((reps,) + (1,) * (t.dim() - 1))[:B].contiguous()
     inp = dict(base)
     inp["batch"] = B
+    strides = None
+    if args.layout == "interleaved":
+        dev, strides = interleave_cache(dev, B, inp["N"], inp["Hkv"], inp["D"])
     algo_code = qsa.QSA_ATTEND_MATRIX if args.algo == "matrix" else qsa.QSA_ATTEND_VECTOR
-    path = qsa.path_for(inp, P=P, algo=algo_code)
+    path = qsa.path_for(inp, P=P, algo=algo_code, strides=strides)
     # The step's new tokens (fp32 K / V / index rows, seeded) and their append.
     gen = torch.Generator(device="cuda").manual_seed(4321)
     T_new = inp["T"]
@@ -286,7 +432,7 @@ def main() -> None:
     v_new = torch.randn((B, T_new, inp["Hkv"], inp["D"]), generator=gen, device="cuda")
     i_new = torch.randn((B, T_new, inp["di"]), generator=gen, device="cuda")
     adesc = qsa.append_desc(batch=B, T=T_new, n_cells=inp["N"], pos0=inp["pos0"],
-                            Hkv=inp["Hkv"], D=inp["D"], d_idx=inp["di"])
+                            Hkv=inp["Hkv"], D=inp["D"], d_idx=inp["di"], strides=strides)
     gate = torch.randn(tuple(dev["q"].shape), generator=gen, device="cuda").to(dev["q"].dtype)
     dev["gate"] = gate
 
@@ -347,7 +493,7 @@ def main() -> None:
         roof = dict(kernel="k_attend", bound="alu", achieved=round(achieved, 2),
                     peak=round(FP32_VALU_PEAK_TFLOPS, 1), unit="TFLOP/s",
                     frac=round(achieved / FP32_VALU_PEAK_TFLOPS, 4),
-                    traffic=profiled_traffic(args.workload, B, P, args.algo),
+                    traffic=profiled_traffic(args.workload, B, P, args.algo, args.layout),
                     algorithmic_bytes=by["attend"],
                     hbm_gbs=round(by["attend"] / (att_ms * 1e-3) / 1e9, 1))
     elif names[dom] == "attend":
@@ -356,16 +502,18 @@ def main() -> None:
         achieved = by["attend"] / (att_ms * 1e-3) / 1e9
         roof = dict(kernel="k_attend_mma", bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=profiled_traffic(args.workload, B, P, args.algo),
+                    traffic=profiled_traffic(args.workload, B, P, args.algo, args.layout),
                     algorithmic_bytes=by["attend"],
                     definition_tflops=round(flops / (att_ms * 1e-3) / 1e12, 2))
     else:
         sb = {"index_topk": by["index"], "merge_gated": by["out"],
               "kv_append": by["append"]}[names[dom]]
         achieved = sb / (stage_ms[dom] * 1e-3) / 1e9
+        traffic = (profiled_index_traffic(args.workload, B, P, args.algo, args.layout)
+                   if names[dom] == "index_topk" else None)
         roof = dict(kernel=names[dom], bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=None)
+                    traffic=traffic, algorithmic_bytes=sb)
 
     line = {
         "metric": METRIC, "value": cells_per_s, "unit": "cells/s", "n_gpus": 1,
@@ -373,7 +521,8 @@ def main() -> None:
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": desc, "batch": B, "T": inp["T"], "n_cells": inp["N"],
                    "k": inp["k"], "P": P, "d_idx": inp["di"], "heads": f"{inp['Hq']}x{inp['D']}",
-                   "kv_heads": inp["Hkv"], "attend_kernel": args.algo},
+                   "kv_heads": inp["Hkv"], "attend_kernel": args.algo,
+                   "kv_layout": args.layout},
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": by["total"],
         "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(names, stage_ms)},
@@ -386,6 +535,8 @@ def main() -> None:
     }
     if inp["q_dtype"] == "f16":
         line["dtype"] = "f16 in, f32 accumulate"
+    if not args.no_ceiling:
+        line["hbm_ceiling"] = hbm_ceiling(inp, dev, path, B, P, by["attend"], stage_ms[2])
     if not args.no_latency:
         p_lat = LATENCY_P.get(args.workload, P)
         line["latency_b1_us"] = dict(P=p_lat, **single_problem_latency(qsa, base, p_lat, algo_code))

@@ -275,3 +275,22 @@ def test_window_host_checks():
     assert _window_call(pd, idsc, ad, ws=16) == WORKSPACE             # not 256-byte aligned
     # misaligned gate and output
     assert _window_call(pd, idsc, ad, gate=8) == INVALID
+
+
+def test_probe_library_exports():
+    """The bandwidth probe bench.py uses is its own library with exactly its
+    three C entry points."""
+    from top_sparse_attention_score_amd.build import PROBE_LIB
+    assert os.path.exists(PROBE_LIB), "run __graft_entry__.build()"
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == {"hbm_probe_stream", "hbm_probe_gather", "hbm_probe_gather_sink_words"}
+    L = ctypes.CDLL(PROBE_LIB)
+    L.hbm_probe_gather_sink_words.restype = ctypes.c_longlong
+    assert L.hbm_probe_gather_sink_words(256, 2, 4) == 512
+    # invalid arguments are rejected before any launch
+    L.hbm_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_void_p]
+    assert L.hbm_probe_stream(None, 16, 16, 1, None) != 0
+    assert L.hbm_probe_stream(16, 15, 16, 1, None) != 0

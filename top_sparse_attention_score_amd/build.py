@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
+# Bandwidth probe library (measurement only; see csrc/hbm_probe.hip).
+PROBE_SRC = "hbm_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libhbm_probe.so")
 
 SOURCES = ("qsa_api.hip", "qsa_index.hip", "qsa_attend.hip", "qsa_attend_mma.hip", "qsa_append.hip",
            "qsa_window.hip")
@@ -51,7 +54,21 @@ def build() -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    """Compile and link libhbm_probe.so (the HBM read-rate probe)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
