@@ -18,8 +18,15 @@
 //                cross-lane reduction.
 //   k_scan_select one token with a row of at most 16384 cells (decode):
 //                scan and select fused in one workgroup per token.
-//   k_idx_gemm   prompt chunk (T > 16): [T x d_idx] x [d_idx x N] on MFMA
-//                (v_mfma_f32_16x16x32_f16), 64 tokens x 256 cells per wave.
+//   k_idx_sample, k_sel_thresh, k_idx_collect, k_sel_cand
+//                many tokens (T > 16, e.g. a prompt chunk) against rows of
+//                16384 to 65536 cells: the score GEMM on MFMA keeps only the
+//                cells at or above a sampled bound, then an exact select
+//                among them; the score matrix is never written (see the
+//                section "many tokens: fused select").
+//   k_idx_gemm   other many-token calls: [T x d_idx] x [d_idx x N] on MFMA
+//                (v_mfma_f32_16x16x32_f16), 64 tokens x 256 cells per wave,
+//                all score keys written for the select below.
 //   k_sel_row    exact top-k of rows up to 65536 cells, one workgroup per
 //                token, keys in registers.
 //   k_sel_*      exact top-k over the score keys of longer rows, tiled over
