@@ -108,3 +108,87 @@ def test_fused_index_fallbacks(orc):
     r_ids, r_ns = _oracle_ids(orc, inp)
     assert_ids_equal(ids, ns, r_ids, r_ns)
     assert np.all(np.isin(planted, r_ids[1, 0, :2048]))
+
+
+# One token against rows longer than the register select holds (65,537 to
+# 262,144 cells): sampled bound, the scan keeping only candidates, exact
+# select among them.  The attention shape is shrunk (the index path does not
+# read it) to keep the inputs small.
+SMALL_KV = dict(Hq=4, Hkv=1, D=64)
+
+
+@pytest.mark.parametrize("cfg,N,pos0,batch,grid", [
+    ("long", 262144, 262143, 2, True),      # the long workload's rows (planted heavy tail)
+    ("long", 262144, 262143, 1, False),     # raw fp16 keys
+    ("decode", 100000, 99999, 3, True),
+    ("decode", 262144, 70000, 1, True),     # visible part of the row only
+    ("decode", 131072, 65536, 2, True),     # just past the register select
+    ("tiny", 80000, 79999, 2, True),        # d_idx 64, k 128
+])
+def test_long_row_index_matches_oracle(orc, cfg, N, pos0, batch, grid):
+    inp = make_inputs(cfg, seed=9500 + batch, batch=batch, N=N, pos0=pos0, index_grid=grid,
+                      **(SMALL_KV if cfg != "tiny" else {}))
+    say(f"[long-row index] {cfg} N={N} pos0={pos0} B={batch} grid={grid}")
+    ids, ns = _gpu_ids(inp)
+    r_ids, r_ns = _oracle_ids(orc, inp)
+    if grid:
+        assert_ids_equal(ids, ns, r_ids, r_ns)
+    else:
+        n_diff = _bounded_ids(inp, ids, ns, r_ids, r_ns)
+        say(f"[long-row index] raw fp16: {n_diff} ids differ, all within the bound")
+
+
+def _bounded_ids(inp, ids, ns, r_ids, r_ns):
+    """General fp16 keys: an id may differ from the oracle's only for a cell
+    whose double score lies within 2 gamma_d max_j sum_i |q_i k_ji| of the
+    k-th double score (fp32 summation bound); returns the differing ids."""
+    di = inp["q_idx"].shape[-1]
+    u = 2.0 ** -24
+    g2 = 2.0 * di * u / (1.0 - di * u)
+    assert np.array_equal(ns, r_ns)
+    n_diff = 0
+    for b in range(ids.shape[0]):
+        for t in range(ids.shape[1]):
+            n = int(ns[b, t])
+            kept, want = ids[b, t, :n], r_ids[b, t, :n]
+            assert np.all(ids[b, t, n:] == -1) and np.all(np.diff(kept) > 0)
+            if np.array_equal(kept, want):
+                continue
+            nvis = inp["pos0"] + t + 1
+            q = inp["q_idx"][b, t].astype(np.float64)
+            K = inp["K_idx"][b, :nvis].astype(np.float64)
+            sc = K @ q
+            slack = g2 * (np.abs(K) @ np.abs(q)).max()
+            diff = np.setxor1d(kept, want)
+            assert np.abs(sc[diff] - sc[want].min()).max() <= slack
+            n_diff += len(diff)
+    return n_diff
+
+
+def test_long_row_fallbacks(orc):
+    """Problem 0: a zero index query (every score equal): the candidate list
+    overflows and the row is scored and selected whole.  Problem 1: 1000
+    sampled cells planted above all others: the bound keeps fewer than k
+    candidates.  Problem 2: four score values, a large exact tie at the k-th
+    inside the candidate list.  Problem 3 takes the normal path."""
+    N = 262144
+    pos0 = N - 1
+    inp = make_inputs("long", seed=9600, batch=4, N=N, pos0=pos0, **SMALL_KV)
+    rng = np.random.default_rng(9601)
+    inp["q_idx"][0] = 0
+    cells = _sample_cells(pos0 + 1)
+    assert len(np.unique(cells)) == 2048 and cells.max() <= pos0
+    inp["K_idx"][1] = np.clip(inp["K_idx"][1], -1, 1)
+    inp["q_idx"][1] = np.abs(inp["q_idx"][1])
+    planted = cells[:1000]
+    inp["K_idx"][1, planted] += np.float16(3.0)
+    inp["q_idx"][2] = 0
+    inp["q_idx"][2, :, 0] = 1.0
+    inp["K_idx"][2] = 0
+    inp["K_idx"][2, :, 0] = rng.choice(np.array([0.0, 1.0, 2.0, 3.0], np.float16), size=N,
+                                       p=[0.5, 0.4925, 0.006, 0.0015])
+    say("[long-row index] fallbacks: all equal, planted sample, 4-valued ties")
+    ids, ns = _gpu_ids(inp)
+    r_ids, r_ns = _oracle_ids(orc, inp)
+    assert_ids_equal(ids, ns, r_ids, r_ns)
+    assert np.all(np.isin(planted, r_ids[1, 0, :2048]))

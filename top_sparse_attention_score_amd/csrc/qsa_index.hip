@@ -24,6 +24,10 @@
 //                cells at or above a sampled bound, then an exact select
 //                among them; the score matrix is never written (see the
 //                section "many tokens: fused select").
+//   k_scan_collect  one token against rows of 65537 to 262144 cells (long
+//                context): the k_idx_scan stream keeping only the cells at or
+//                above a sampled bound (k_idx_sample, k_sel_thresh), then
+//                k_sel_cand's exact select among them.
 //   k_idx_gemm   other many-token calls: [T x d_idx] x [d_idx x N] on MFMA
 //                (v_mfma_f32_16x16x32_f16), 64 tokens x 256 cells per wave,
 //                all score keys written for the select below.
@@ -899,6 +903,9 @@ constexpr int kCandCap = 8192;        // candidates kept per token
 constexpr int kCollectList = 64;      // LDS candidate slots per (workgroup, token)
 constexpr int kFusedMaxCells = 65536; // longest row of the fused path (bitmap, registers)
 constexpr int kFusedMinCells = 16384; // shorter rows write their keys instead
+// One-token rows between the register select's limit and this length take
+// the sampled-bound path with k_scan_collect (bitmap of the row in LDS).
+constexpr int kLongFusedMaxCells = 262144;
 
 // Reduction-index permutation of the matrix-core score kernels: at step st,
 // lane group g (lanes 16g .. 16g+15) supplies row elements
@@ -1213,9 +1220,83 @@ __global__ __launch_bounds__(256) void k_idx_collect(const _Float16* __restrict_
     }
 }
 
+// One token (T = 1) against a long row: the chip-wide scan of k_idx_scan,
+// keeping only the (score, cell) pairs at or above the problem's bound
+// instead of writing every key.  A workgroup scans kScanCollectSpan row
+// blocks and stages its candidates in LDS, so the problem's list takes one
+// atomic per workgroup (same-address device atomics are slow); a full LDS
+// list spills straight to the problem's list until that overflows.  Grid
+// (ceil(row blocks / kScanCollectSpan), B).
+constexpr int kScanCollectSpan = 4;
+constexpr int kScanCollectList = 512;
+
+template <int DI>
+__global__ __launch_bounds__(256) void k_scan_collect(const uint4* __restrict__ q_idx,
+                                                      const uint4* __restrict__ K_idx,
+                                                      const uint32_t* __restrict__ thr,
+                                                      uint32_t* __restrict__ gcount,
+                                                      uint2* __restrict__ cand, int N, int nvis)
+{
+    constexpr int RB = idx_scan_rows_per_block<DI>();
+    __shared__ uint2 lst[kScanCollectList];
+    __shared__ uint32_t s_cnt, s_base;
+    const int b = blockIdx.y;
+    const float bound = key_to_score(thr[b]);   // score_key(s) >= thr  <=>  s >= bound
+    uint32_t* gc = gcount + b;
+    uint2* list = cand + (size_t)b * kCandCap;
+    if (threadIdx.x == 0)
+        s_cnt = 0u;
+    __syncthreads();
+    bool full = false;   // this lane saw the problem's list overflow
+    const int nrb = (nvis + RB - 1) / RB;
+    const int bx0 = blockIdx.x * kScanCollectSpan;
+    const int nb = min(kScanCollectSpan, nrb - bx0);
+    uint4 qv[1];
+    idx_scan_query<DI, 1>(b, q_idx, 1, qv);
+    auto emit = [&](int, int j, float sc) {
+        if (sc >= bound) {
+            const uint2 e = make_uint2(__float_as_uint(sc), (uint32_t)j);
+            const uint32_t slot = atomicAdd(&s_cnt, 1u);
+            if (slot < (uint32_t)kScanCollectList) {
+                lst[slot] = e;
+            } else if (!full) {
+                const uint32_t p = atomicAdd(gc, 1u);
+                if (p < (uint32_t)kCandCap)
+                    list[p] = e;
+                else
+                    full = true;
+            }
+        }
+    };
+    // Row blocks in turn, the next block's keys in flight while the current
+    // one is scored (two register buffers, alternating).
+    uint4 ka[kScanSteps], kb[kScanSteps];
+    idx_scan_load<DI>(bx0, b, K_idx, N, nvis, ka);
+#pragma unroll 1
+    for (int i = 0; i < nb; i += 2) {
+        if (i + 1 < nb)
+            idx_scan_load<DI>(bx0 + i + 1, b, K_idx, N, nvis, kb);
+        idx_scan_compute<DI, 1>(bx0 + i, qv, ka, 1, nvis, emit);
+        if (i + 1 >= nb)
+            break;
+        if (i + 2 < nb)
+            idx_scan_load<DI>(bx0 + i + 2, b, K_idx, N, nvis, ka);
+        idx_scan_compute<DI, 1>(bx0 + i + 1, qv, kb, 1, nvis, emit);
+    }
+    __syncthreads();
+    const uint32_t n = min(s_cnt, (uint32_t)kScanCollectList);
+    if (threadIdx.x == 0)
+        s_base = n ? atomicAdd(gc, n) : 0u;
+    __syncthreads();
+    const uint32_t base = s_base;
+    for (uint32_t i = threadIdx.x; i < n; i += 256)
+        if (base + i < (uint32_t)kCandCap)
+            list[base + i] = lst[i];
+}
+
 // One workgroup per token: the exact top-k among its candidates, or the
 // whole-row fallback (see above).
-template <int DI>
+template <int DI, int MAXC, bool SCAN1>
 __global__ __launch_bounds__(kSelThreads) void k_sel_cand(const _Float16* __restrict__ q_idx,
                                                           const _Float16* __restrict__ K_idx,
                                                           const uint32_t* __restrict__ gcount,
@@ -1227,12 +1308,12 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_cand(const _Float16* __rest
                                                           int cap)
 {
     constexpr int CPT = kCandCap / kSelThreads;    // candidates per thread
-    constexpr int WPT = kFusedMaxCells / 32 / kSelThreads;   // bitmap words per thread
+    constexpr int WPT = MAXC / 32 / kSelThreads;   // bitmap words per thread
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t s_wave[kSelThreads / 64];
     __shared__ uint32_t s_pick[2];
     __shared__ uint32_t s_red[8];
-    __shared__ uint32_t bm[kFusedMaxCells / 32];
+    __shared__ uint32_t bm[MAXC / 32];
     const int bt = blockIdx.x, tid = threadIdx.x;
     const int nvis = pos0 + bt % T + 1;
     int32_t* out = ids + (size_t)bt * cap;
@@ -1374,8 +1455,20 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_cand(const _Float16* __rest
         return;
     }
 
-    // Fallback: the whole row again (as k_idx_collect computes it) into the
-    // token's key row, then the exact select over that row.
+    // Fallback: the whole row again (with the arithmetic of the kernel that
+    // collected the candidates) into the token's key row, then the exact
+    // select over that row.
+    uint32_t* kr = keys + (size_t)bt * N;
+    if constexpr (SCAN1) {
+        constexpr int RB = idx_scan_rows_per_block<DI>();
+        for (int bx = 0; bx * RB < nvis; ++bx)
+            idx_scan_block<DI, 1>(bx, bt, (const uint4*)q_idx, (const uint4*)K_idx, keys, 1, N,
+                                  nvis);
+        __threadfence_block();
+        __syncthreads();
+        select_row_stream(kr, nvis, k, cap, out, n_sel + bt, hist, s_red, s_wave, s_pick);
+        return;
+    }
     constexpr int KS = DI / 32;
     const int lane = tid & 63, wv = tid >> 6, r = lane & 15, grp = lane >> 4;
     const int b = bt / T;
@@ -1383,7 +1476,6 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_cand(const _Float16* __rest
 #pragma unroll
     for (int st = 0; st < KS; ++st)
         qt[st] = *(const h8_t*)(q_idx + (size_t)bt * DI + kperm(st, grp));
-    uint32_t* kr = keys + (size_t)bt * N;
     for (int c0 = 16 * wv; c0 < nvis; c0 += 16 * (kSelThreads / 64)) {
         const int cell = min(c0 + r, nvis - 1);
         const _Float16* src = K_idx + ((size_t)b * N + cell) * DI;
@@ -1440,7 +1532,8 @@ static SelWs carve(void* ws, int B, int T, int N, size_t* total)
     w.cand = (uint32_t*)take(BT * kCap * 8);
     w.pivot = (uint32_t*)take(BT * 8);
     // fused many-token path (k_idx_sample .. k_sel_cand)
-    const bool fused = T > 16 && N <= kFusedMaxCells;
+    const bool fused = (T > 16 && N <= kFusedMaxCells) ||
+                       (T == 1 && N > kRowThreads * 64 && N <= kLongFusedMaxCells);
     w.thr = (uint32_t*)take(fused ? BT * 4 : 0);
     w.gcount = (uint32_t*)take(fused ? BT * 4 : 0);
     w.samp = (uint32_t*)take(fused ? BT * kSampleCells * 4 : 0);
@@ -1517,7 +1610,8 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
                                             a.dense_max);                                     \
     k_idx_collect<DI><<<gc, 256, 0, s>>>(q, K, w.thr, w.gcount, w.fcand, a.T, a.N, a.pos0, n_cr, \
                                          n_tb, a.B);                                          \
-    k_sel_cand<DI><<<BT, kSelThreads, 0, s>>>(q, K, w.gcount, w.fcand, w.keys, a.ids, a.n_sel,  \
+    k_sel_cand<DI, kFusedMaxCells, false><<<BT, kSelThreads, 0, s>>>(                          \
+        q, K, w.gcount, w.fcand, w.keys, a.ids, a.n_sel,                                      \
                                               a.T, a.N, a.pos0, a.k, a.dense_max, a.cap)
         if (a.DI == 64) {
             QSA_FUSED(64);
@@ -1525,6 +1619,34 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
             QSA_FUSED(128);
         }
 #undef QSA_FUSED
+        return hipGetLastError();
+    }
+    // One token against a row too long for the register select: sampled
+    // bound, then the chip-wide scan keeps only the candidates, then the
+    // exact select among them (no key array, no chip-wide select).
+    const bool long1 = any_select && a.T == 1 && a.N > kRowThreads * 64 &&
+                       a.N <= kLongFusedMaxCells && a.k <= kCandCap / 2;
+    if (long1) {
+        const dim3 gs(kSampleCells / 256, 1, a.B);
+        const _Float16* q = (const _Float16*)a.q_idx;
+        const _Float16* K = (const _Float16*)a.K_idx;
+#define QSA_LONG1(DI)                                                                          \
+    k_idx_sample<DI><<<gs, 256, 0, s>>>(q, K, w.samp, 1, a.N, a.pos0, nvis_max);               \
+    k_sel_thresh<<<a.B, kSelThreads, 0, s>>>(w.samp, w.thr, w.gcount, 1, a.pos0, a.k,           \
+                                             a.dense_max);                                    \
+    k_scan_collect<DI><<<dim3((nvis_max + idx_scan_rows_per_block<DI>() * kScanCollectSpan -   \
+                               1) / (idx_scan_rows_per_block<DI>() * kScanCollectSpan),       \
+                              a.B),                                                            \
+                         256, 0, s>>>((const uint4*)a.q_idx, (const uint4*)a.K_idx, w.thr,     \
+                                      w.gcount, w.fcand, a.N, nvis_max);                       \
+    k_sel_cand<DI, kLongFusedMaxCells, true><<<a.B, kSelThreads, 0, s>>>(                      \
+        q, K, w.gcount, w.fcand, w.keys, a.ids, a.n_sel, 1, a.N, a.pos0, a.k, a.dense_max, a.cap)
+        if (a.DI == 64) {
+            QSA_LONG1(64);
+        } else {
+            QSA_LONG1(128);
+        }
+#undef QSA_LONG1
         return hipGetLastError();
     }
     if (any_select) {

@@ -40,32 +40,49 @@ __device__ __forceinline__ float row_sum(float v)
 // 16 bytes each, so every load instruction of a wave covers 64/LPR whole,
 // consecutive rows: fully coalesced.  Each lane keeps the 8 index-query
 // values of its slice for all T tokens in registers.  Workgroup (bx, b)
-// covers rows bx * 64 * 8 * 256 / DI .. of problem b.
-template <int DI, int TT>
-__device__ __forceinline__ void idx_scan_block(int bx, int b, const uint4* __restrict__ q_idx,
-                                               const uint4* __restrict__ K_idx,
-                                               uint32_t* __restrict__ keys, int T, int N,
-                                               int nvis_max)
+// covers rows bx * 64 * 8 * 256 / DI .. of problem b; the first lane of each
+// row calls emit(t, row, score) for every visible row and token.
+constexpr int kScanSteps = 8;   // row steps in flight per thread (U)
+
+// The key loads of workgroup bx of idx_scan_rows (rows past nvis_max repeat
+// the last visible row).
+template <int DI>
+__device__ __forceinline__ void idx_scan_load(int bx, int b, const uint4* __restrict__ K_idx,
+                                              int N, int nvis_max, uint4 (&kv)[kScanSteps])
 {
-    constexpr int LPR = DI / 8;           // lanes per row
-    constexpr int RPI = 256 / LPR;        // rows per block-wide step
-    constexpr int U = 8;                  // steps in flight per thread
+    constexpr int LPR = DI / 8, RPI = 256 / LPR;
     const int sub = threadIdx.x % LPR;
-    const int r0 = bx * (RPI * U) + threadIdx.x / LPR;
-
-    uint4 qv[TT];
+    const int r0 = bx * (RPI * kScanSteps) + threadIdx.x / LPR;
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
-        qv[t] = (t < T) ? q_idx[((size_t)b * T + t) * (DI / 8) + sub] : make_uint4(0, 0, 0, 0);
-
-    uint4 kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kScanSteps; ++u) {
         const int j = min(r0 + u * RPI, nvis_max - 1);
         kv[u] = K_idx[((size_t)b * N + j) * (DI / 8) + sub];
     }
+}
+
+// The index-query slice of this lane for tokens 0..T-1 (TT at most).
+template <int DI, int TT>
+__device__ __forceinline__ void idx_scan_query(int b, const uint4* __restrict__ q_idx, int T,
+                                               uint4 (&qv)[TT])
+{
+    const int sub = threadIdx.x % (DI / 8);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int t = 0; t < TT; ++t)
+        qv[t] = (t < T) ? q_idx[((size_t)b * T + t) * (DI / 8) + sub] : make_uint4(0, 0, 0, 0);
+}
+
+// Scores of the rows loaded by idx_scan_load: emit(t, row, score) from the
+// first lane of each visible row.
+template <int DI, int TT, class Emit>
+__device__ __forceinline__ void idx_scan_compute(int bx, const uint4 (&qv)[TT],
+                                                 const uint4 (&kv)[kScanSteps], int T,
+                                                 int nvis_max, Emit emit)
+{
+    constexpr int LPR = DI / 8, RPI = 256 / LPR;
+    const int sub = threadIdx.x % LPR;
+    const int r0 = bx * (RPI * kScanSteps) + threadIdx.x / LPR;
+#pragma unroll
+    for (int u = 0; u < kScanSteps; ++u) {
         const int j = r0 + u * RPI;
         const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
 #pragma unroll
@@ -78,10 +95,40 @@ __device__ __forceinline__ void idx_scan_block(int bx, int b, const uint4* __res
                     acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
                 acc = row_sum<LPR>(acc);
                 if (sub == 0 && j < nvis_max)
-                    keys[((size_t)b * T + t) * N + j] = score_key(acc);
+                    emit(t, j, acc);
             }
         }
     }
+}
+
+template <int DI, int TT, class Emit>
+__device__ __forceinline__ void idx_scan_rows(int bx, int b, const uint4* __restrict__ q_idx,
+                                              const uint4* __restrict__ K_idx, int T, int N,
+                                              int nvis_max, Emit emit)
+{
+    uint4 qv[TT];
+    idx_scan_query<DI, TT>(b, q_idx, T, qv);
+    uint4 kv[kScanSteps];
+    idx_scan_load<DI>(bx, b, K_idx, N, nvis_max, kv);
+    idx_scan_compute<DI, TT>(bx, qv, kv, T, nvis_max, emit);
+}
+
+// Rows a workgroup of idx_scan_rows covers.
+template <int DI>
+constexpr int idx_scan_rows_per_block()
+{
+    return (256 / (DI / 8)) * kScanSteps;
+}
+
+template <int DI, int TT>
+__device__ __forceinline__ void idx_scan_block(int bx, int b, const uint4* __restrict__ q_idx,
+                                               const uint4* __restrict__ K_idx,
+                                               uint32_t* __restrict__ keys, int T, int N,
+                                               int nvis_max)
+{
+    idx_scan_rows<DI, TT>(bx, b, q_idx, K_idx, T, N, nvis_max, [&](int t, int j, float sc) {
+        keys[((size_t)b * T + t) * N + j] = score_key(sc);
+    });
 }
 
 __host__ __device__ __forceinline__ bool token_selects(int nvis, int k, int dense_max)
