@@ -1,19 +1,30 @@
 """Throughput benchmark of the QSA hot path on one MI355X.
 
-One step = qsa_kv_append -> qsa_index_topk -> qsa_attend -> qsa_merge_gated
-over a batch of B independent problems (seeded synthetic caches already
-resident in HBM): the step's T new tokens are quantised into their cells of
-the cache, then selected from and attended to, and the merged output is
-gated.
+One step = append -> index_topk -> attend -> gated merge over a batch of B
+independent problems (seeded synthetic caches already resident in HBM): the
+step's T new tokens are quantised into their cells of the cache, then
+selected from and attended to, and the merged output is gated.  The step is
+one qsa_step call, which runs those four calls in the fewest kernel launches
+the shape allows (the append inside the decode scan/select kernel, the merge
+inside the attention kernel when P is 1, 2 or 4); --merge separate times the
+four calls one by one instead.
 The default workload is the decode step (1 token, 24 x 256 query heads,
 2 KV heads, 8192 cached cells, index dim 128, top-2048) over B = 256
 independent caches, so the working set (~2.7 GB) is far larger than the
 256 MB last-level cache and every step streams from HBM.
 
+Timing: the K timed steps run back to back between two HIP events on the
+launch stream (nothing else is enqueued between them); four more such
+blocks give the median/min/max over rounds.  A separate pass of the same
+calls one by one, with an event between stages, gives the per-stage
+breakdown (each event adds a few microseconds of its own), and the
+roofline's kernel time is the average of ten back-to-back launches of the
+dominant stage.
+
 Prints one JSON line: metric/value (kept KV cells attended per second),
-per-stage times from HIP events recorded on the launch stream, algorithmic
-HBM bytes and flops, the roofline of the dominant kernel, and the oracle's
-single-thread throughput on a bounded sample of the same workload.
+stage times, algorithmic HBM bytes and flops, the roofline of the dominant
+kernel, and the oracle's throughput on a bounded sample of the same
+workload on the host's cores.
 """
 from __future__ import annotations
 
@@ -79,7 +90,8 @@ def attend_flops(p: dict, n_sel_total: int) -> float:
 
 # Source file of each attend kernel family (its hash gates profiled traffic).
 ATTEND_SOURCES = {"matrix": "qsa_attend_mma.hip", "vector": "qsa_attend.hip"}
-ATTEND_KERNELS = {"matrix": "k_attend_mma", "vector": "k_attend"}
+ATTEND_KERNELS = {"matrix": "k_attend_mma", "vector": "k_attend",
+                  "matrix_merge": "k_attend_merge_mma"}
 # Headers whose code the attend kernels compile in (also hashed).
 ATTEND_HEADERS = ("qsa_device.h", "qsa_mma.h", "qsa_attend_mma.h", "qsa_merge.h")
 # Source and headers of the index kernels (their hash gates profiled index
@@ -120,6 +132,7 @@ def profiled_index_traffic(workload: str, B: int, P: int, algo: str, layout: str
 
 
 def profiled_traffic(workload: str, B: int, P: int, algo: str, layout: str = "dense"):
+    src_algo = "matrix" if algo == "matrix_merge" else algo
     """HBM bytes per attend dispatch from the committed rocprofv3 summary of
     this exact launch configuration
     (profiles/<kernel>_<workload>_b<B>_P<P>[_<layout>].md), scaled by the
@@ -127,7 +140,7 @@ def profiled_traffic(workload: str, B: int, P: int, algo: str, layout: str = "de
     or the kernel source (with the device headers it includes) changed since
     it was taken."""
     f = _profile_fields(workload, B, P, algo, layout)
-    if f.get("traffic_source_sha256_16") != source_hash((ATTEND_SOURCES[algo],) +
+    if f.get("traffic_source_sha256_16") != source_hash((ATTEND_SOURCES[src_algo],) +
                                                         ATTEND_HEADERS):
         return None
     try:
@@ -373,7 +386,7 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--P", type=int, default=None)
@@ -387,6 +400,9 @@ def main() -> None:
                     help="qsa_attend kernel family")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the attainable-HBM-rate probes")
+    ap.add_argument("--merge", default="fused", choices=["fused", "separate"],
+                    help="attention and gated merge as one kernel (qsa_attend_merge, where "
+                         "P is 1, 2 or 4) or as qsa_attend + qsa_merge_gated")
     ap.add_argument("--layout", default="interleaved", choices=["dense", "interleaved"],
                     help="KV cache layout: dense arrays [B][N][Hkv][D] and [B][N][Hkv][D/32], "
                          "or one row per cell holding every head's K codes, V codes, K "
@@ -439,6 +455,22 @@ def main() -> None:
     def append():
         qsa.qsa_kv_append(adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"], dev["Vq"],
                           dev["Vsc"], dev["K_idx"])
+
+    fused = args.merge == "fused" and args.algo == "matrix" and P in (1, 2, 4)
+
+    def attend_and_merge(ev=None):
+        """attention + gated merge: one fused kernel, or the two calls (the
+        event between them, if given, splits the two stages)."""
+        if fused:
+            path.attend_merge(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"],
+                              gate=gate)
+            if ev is not None:
+                ev.record(stream)
+        else:
+            path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"])
+            if ev is not None:
+                ev.record(stream)
+            path.merge(gate=gate)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 18        # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -451,42 +483,91 @@ def main() -> None:
 
     stream = torch.cuda.current_stream()
     K, W = args.steps, args.warmup
+    # The step: one qsa_step call (append -> index -> attend -> gated merge
+    # in the fewest launches the shape allows), marshalled once.
+    ws_step = torch.empty(qsa.qsa_step_workspace(path.idesc, path.adesc) // 4 + 64,
+                          dtype=torch.int32, device="cuda")
+    step = qsa.StepCall(adesc, path.idesc, path.adesc, k_new, v_new, i_new, dev["Kq"],
+                        dev["Ksc"], dev["Vq"], dev["Vsc"], dev["K_idx"], dev["q_idx"], dev["q"],
+                        gate, path.ids, path.n_sel, path.out, ws_step, stream)
+    if args.merge == "separate" or args.algo != "matrix":
+        def step():  # noqa: F811  (the four calls, one by one)
+            append()
+            path.index(dev["q_idx"], dev["K_idx"])
+            attend_and_merge()
     for _ in range(W):
-        append()
-        path.run(dev)
+        step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    t_start = time.perf_counter()
-    for s in range(K):
-        e = evs[s]
-        e[0].record(stream)
-        append()
-        e[1].record(stream)
-        path.index(dev["q_idx"], dev["K_idx"])
-        e[2].record(stream)
-        path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"])
-        e[3].record(stream)
-        path.merge(gate=gate)
-        e[4].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    stage = np.zeros(4)
-    for e in evs:
-        for i in range(4):
-            stage[i] += e[i].elapsed_time(e[i + 1])
-    stage_ms = stage / K
-    step_ms = float(evs[0][0].elapsed_time(evs[-1][4])) / K
-    per_step_us = np.array([e[0].elapsed_time(e[4]) * 1e3 for e in evs])
-
     n_sel_total = int(path.n_sel.sum().item())
     by = algorithmic_bytes(inp, B, n_sel_total)
+    fused_att_bytes = by["attend"] + (by["out"] if fused else 0)
+
+    def kernel_ms(fn, n=10):
+        """Average duration of n back-to-back launches of one call on the
+        launch stream (events around the n launches only)."""
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def attend_call():
+        if fused:
+            path.attend_merge(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"], gate=gate)
+        else:
+            path.attend(dev["q"], dev["Kq"], dev["Ksc"], dev["Vq"], dev["Vsc"])
+
+    # Attainable read rates of this GPU, measured before the timed steps (the
+    # probes also bring the GPU to its working clocks).
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = hbm_ceiling(inp, dev, path, B, P, fused_att_bytes,
+                              kernel_ms(attend_call))
+        for _ in range(W):
+            step()
+
+    def timed_block():
+        """K steps between two events on the launch stream (nothing else
+        enqueued between them); microseconds per step."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(K):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
+
+    t_start = time.perf_counter()
+    step_us0 = timed_block()                    # the reported K steps
+    wall = time.perf_counter() - t_start
+    rounds_us = np.array([step_us0] + [timed_block() for _ in range(4)])
+    step_ms = step_us0 * 1e-3
+
+    # Stage breakdown: each of the step's calls on its own, as the average of
+    # ten back-to-back launches (every call is idempotent on these buffers:
+    # the append rewrites the same cells with the same values).
+    stage_ms = np.array([kernel_ms(append), kernel_ms(lambda: path.index(dev["q_idx"],
+                                                                         dev["K_idx"])),
+                         kernel_ms(attend_call),
+                         0.0 if fused else kernel_ms(lambda: path.merge(gate=gate))])
+
     flops = attend_flops(inp, n_sel_total)
     cells_per_s = n_sel_total / (step_ms * 1e-3)
     gbs = by["total"] / (step_ms * 1e-3) / 1e9
 
-    # Dominant kernel: the stage with the largest average time.
+    # Dominant kernel: the stage with the largest average time.  With the
+    # fused kernel the attend stage includes the gated merge (its bytes: the
+    # gate read and the output written) and the merge stage is empty.
     names = ["kv_append", "index_topk", "attend", "merge_gated"]
+    if fused:
+        names[2] = "attend_merge_gated"
     dom = int(np.argmax(stage_ms))
+    att_bytes = fused_att_bytes
     att_ms = stage_ms[2]
     if names[dom] == "attend" and args.algo == "vector":
         achieved = flops / (att_ms * 1e-3) / 1e12
@@ -496,14 +577,15 @@ def main() -> None:
                     traffic=profiled_traffic(args.workload, B, P, args.algo, args.layout),
                     algorithmic_bytes=by["attend"],
                     hbm_gbs=round(by["attend"] / (att_ms * 1e-3) / 1e9, 1))
-    elif names[dom] == "attend":
+    elif dom == 2:
         # Matrix kernel: the products run on the matrix cores far below
         # their peak; the gathers of the kept cells bound it.
-        achieved = by["attend"] / (att_ms * 1e-3) / 1e9
-        roof = dict(kernel="k_attend_mma", bound="hbm", achieved=round(achieved, 1),
+        kalgo = "matrix_merge" if fused else "matrix"
+        achieved = att_bytes / (att_ms * 1e-3) / 1e9
+        roof = dict(kernel=ATTEND_KERNELS[kalgo], bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=profiled_traffic(args.workload, B, P, args.algo, args.layout),
-                    algorithmic_bytes=by["attend"],
+                    traffic=profiled_traffic(args.workload, B, P, kalgo, args.layout),
+                    algorithmic_bytes=att_bytes,
                     definition_tflops=round(flops / (att_ms * 1e-3) / 1e12, 2))
     else:
         sb = {"index_topk": by["index"], "merge_gated": by["out"],
@@ -522,21 +604,24 @@ def main() -> None:
         "config": {"workload": desc, "batch": B, "T": inp["T"], "n_cells": inp["N"],
                    "k": inp["k"], "P": P, "d_idx": inp["di"], "heads": f"{inp['Hq']}x{inp['D']}",
                    "kv_heads": inp["Hkv"], "attend_kernel": args.algo,
+                   "merge": "fused" if fused else "separate",
                    "kv_layout": args.layout},
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": by["total"],
-        "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(names, stage_ms)},
-        "step_us": {"mean": round(step_ms * 1e3, 2),
-                    "median": round(float(np.median(per_step_us)), 2),
-                    "min": round(float(per_step_us.min()), 2),
-                    "max": round(float(per_step_us.max()), 2)},
+        "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(names, stage_ms)
+                     if not (fused and n == "merge_gated")},
+        "step_us": {"timed": round(step_us0, 2), "rounds": len(rounds_us),
+                    "median": round(float(np.median(rounds_us)), 2),
+                    "min": round(float(rounds_us.min()), 2),
+                    "max": round(float(rounds_us.max()), 2)},
+        "launch": "qsa_step" if step.__class__.__name__ == "StepCall" else "separate calls",
         "wall_s": round(wall, 3),
         "roofline": roof,
     }
     if inp["q_dtype"] == "f16":
         line["dtype"] = "f16 in, f32 accumulate"
-    if not args.no_ceiling:
-        line["hbm_ceiling"] = hbm_ceiling(inp, dev, path, B, P, by["attend"], stage_ms[2])
+    if ceiling is not None:
+        line["hbm_ceiling"] = ceiling
     if not args.no_latency:
         p_lat = LATENCY_P.get(args.workload, P)
         line["latency_b1_us"] = dict(P=p_lat, **single_problem_latency(qsa, base, p_lat, algo_code))

@@ -263,6 +263,30 @@ QSA_API int qsa_merge_gated(const qsa_attn_desc* desc, const float* partials, co
                             void* out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * qsa_attend_merge -- qsa_attend followed by qsa_merge_gated in ONE kernel:
+ * the attention over the kept cells of the "opus r20 ..." page, section 2
+ * (qsa_attn), whose chunk partials are merged by that section's qsa_merge
+ * formula and gated as qsa_merge_gated describes, without writing the
+ * partials to memory.
+ *
+ * Each workgroup of the matrix kernel computes four (token, chunk) items;
+ * when P divides 4 these are all the chunks of whole tokens, so the
+ * workgroup merges its own partials in on-chip memory.  The merge runs the
+ * same operations in the same order as qsa_merge on the same partial
+ * values, so out equals qsa_attend + qsa_merge_gated with the same
+ * arguments bit for bit.
+ *
+ * Arguments: desc, q, Kq, Ksc, Vq, Vsc, ids, n_sel as qsa_attend; gate and
+ * out as qsa_merge_gated (gate NULL: no gate).  No partials are written.
+ * Supported: as qsa_attend, with P in {1, 2, 4} and algo AUTO or MATRIX
+ * (else QSA_ERR_UNSUPPORTED: use the two calls).
+ * --------------------------------------------------------------------- */
+QSA_API int qsa_attend_merge(const qsa_attn_desc* desc, const void* q, const int8_t* Kq,
+                             const void* Ksc, const int8_t* Vq, const void* Vsc,
+                             const int32_t* ids, const int32_t* n_sel, const void* gate,
+                             void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * qsa_kv_append -- write T new tokens into the cache, the step that feeds
  * the path: their K and V rows become int8 codes with one fp16 scale per
  * 32 elements (the cache format of the "opus r20 ..." page, section 3:
@@ -368,6 +392,47 @@ QSA_API int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc
                               int8_t* Vq, void* Vsc, void* K_idx, const void* q_idx,
                               const void* q, const void* gate, int32_t* ids, int32_t* n_sel,
                               void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * qsa_step -- one step of the whole path for every workload shape, in as
+ * few kernel launches as the shape allows: qsa_kv_append of the T new
+ * tokens, then qsa_index_topk, qsa_attend and qsa_merge_gated, each reading
+ * what the one before wrote.
+ *
+ * Every dependent kernel launch costs a few microseconds of idle GPU (the
+ * end of one kernel and the start of the next), so the step folds calls
+ * together where one workgroup already owns everything a call needs:
+ *   - the append runs inside the index kernel when that kernel gives each
+ *     problem one workgroup (one token per problem, batch >= 128, rows of
+ *     at most 16384 cells, some token selecting): that workgroup writes its
+ *     problem's new token, then scans the keys;
+ *   - the merge and the gate run inside the attention kernel when P is 1,
+ *     2 or 4 with the matrix kernel (as qsa_attend_merge).
+ * Otherwise the calls run as their own kernels, in order.  The results
+ * (new cache codes, scales and index keys; ids and n_sel; out) equal those
+ * of the four calls with the same descriptors bit for bit.
+ *
+ * Arguments are those of the four calls: pdesc/k_new/v_new/kidx_new/cache
+ * as qsa_kv_append; idesc/q_idx/K_idx/ids/n_sel as qsa_index_topk; adesc/
+ * q/cache/ids/n_sel as qsa_attend; gate/out as qsa_merge_gated.  The three
+ * descriptors must describe the same step: equal T, batch and n_cells,
+ * pdesc->pos0 == idesc->pos0, equal Hkv and D, equal ids_cap, equal d_idx
+ * when kidx_new is given, and the same resolved cache strides (else
+ * QSA_ERR_INVALID_ARG).  Ksc and Vsc must be 16-byte aligned.
+ *
+ * Workspace: at least qsa_step_workspace(idesc, adesc) bytes (the index
+ * workspace, plus the partials when the merge runs as its own kernel),
+ * 256-byte aligned, contents on entry irrelevant.
+ * Supported: what each of the four calls supports.
+ * --------------------------------------------------------------------- */
+QSA_API size_t qsa_step_workspace(const qsa_index_desc* idesc, const qsa_attn_desc* adesc);
+
+QSA_API int qsa_step(const qsa_append_desc* pdesc, const qsa_index_desc* idesc,
+                     const qsa_attn_desc* adesc, const float* k_new, const float* v_new,
+                     const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc,
+                     void* K_idx, const void* q_idx, const void* q, const void* gate,
+                     int32_t* ids, int32_t* n_sel, void* out, void* ws, size_t ws_bytes,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -160,6 +160,26 @@ def test_merge_gated_checks():
     assert L.qsa_merge_gated(ctypes.byref(_adesc(P=65)), 16, 16, 16, None) == UNSUPPORTED
 
 
+def test_attend_merge_host_checks():
+    """qsa_attend_merge validates like qsa_attend + qsa_merge_gated and
+    rejects splits that one workgroup cannot merge, all before any launch."""
+    L = qb.lib()
+    d = _adesc(P=4)
+    ins = [16] * 7                      # q, Kq, Ksc, Vq, Vsc, ids, n_sel
+    args = ins + [16, 16]               # + gate, out
+    assert L.qsa_attend_merge(None, *args, None) == INVALID
+    assert L.qsa_attend_merge(ctypes.byref(d), None, *args[1:], None) == INVALID  # null q
+    assert L.qsa_attend_merge(ctypes.byref(d), *ins, 16, None, None) == INVALID   # null out
+    assert L.qsa_attend_merge(ctypes.byref(d), *ins, 16, 8, None) == INVALID      # misaligned out
+    assert L.qsa_attend_merge(ctypes.byref(d), *ins, 8, 16, None) == INVALID      # misaligned gate
+    for P in (3, 8, 16, 64):
+        assert L.qsa_attend_merge(ctypes.byref(_adesc(P=P)), *args, None) == UNSUPPORTED
+    assert L.qsa_attend_merge(ctypes.byref(_adesc(P=65)), *args, None) == UNSUPPORTED
+    vec = _adesc(P=4)
+    vec.algo = qb.QSA_ATTEND_VECTOR
+    assert L.qsa_attend_merge(ctypes.byref(vec), *args, None) == UNSUPPORTED
+
+
 def test_null_descriptor():
     L = qb.lib()
     assert L.qsa_index_topk(None, 16, 16, 16, 16, 16, 64, None) == INVALID
@@ -275,6 +295,60 @@ def test_window_host_checks():
     assert _window_call(pd, idsc, ad, ws=16) == WORKSPACE             # not 256-byte aligned
     # misaligned gate and output
     assert _window_call(pd, idsc, ad, gate=8) == INVALID
+
+
+def _step_call(pd, idsc, ad, ws=256, ws_bytes=1 << 30, kidx=16, gate=16):
+    # as _window_call: every case below fails validation, nothing launches
+    return qb.lib().qsa_step(
+        None if pd is None else ctypes.byref(pd), None if idsc is None else ctypes.byref(idsc),
+        None if ad is None else ctypes.byref(ad), 16, 16, kidx, 16, 16, 16, 16, 16, 16, 16,
+        gate, 16, 16, 16, ws, ws_bytes, None)
+
+
+def test_step_workspace_size():
+    """The index workspace, plus the partials only when the merge is not
+    fused into the attention (P outside {1, 2, 4}, or the vector kernel)."""
+    L = qb.lib()
+    _, idsc, _ = _window_descs()
+    iws = L.qsa_index_topk_workspace(ctypes.byref(idsc))
+    fused = L.qsa_step_workspace(ctypes.byref(idsc), ctypes.byref(_adesc(batch=2, P=4)))
+    split = L.qsa_step_workspace(ctypes.byref(idsc), ctypes.byref(_adesc(batch=2, P=8)))
+    vec = L.qsa_step_workspace(ctypes.byref(idsc), ctypes.byref(_adesc(batch=2, P=4, algo=2)))
+    assert iws <= fused < iws + 256
+    rows = 2 * 24 * 8
+    assert split >= fused + rows * (2 + 256) * 4
+    assert vec >= fused + 2 * 24 * 4 * (2 + 256) * 4
+    assert L.qsa_step_workspace(ctypes.byref(_idesc(batch=0)), ctypes.byref(_adesc())) == 0
+    assert L.qsa_step_workspace(ctypes.byref(idsc), ctypes.byref(_adesc(D=48))) == 0
+
+
+def test_step_host_checks():
+    """qsa_step validates the three descriptors, their agreement and the
+    workspace on the host; every rejected call enqueues nothing."""
+    pd, idsc, ad = _window_descs()
+    assert _step_call(None, idsc, ad) == INVALID
+    assert _step_call(pd, None, ad) == INVALID
+    assert _step_call(pd, idsc, None) == INVALID
+    for bad in (dict(pos0=100), dict(batch=3), dict(D=64), dict(Hkv=1),
+                dict(n_cells=8000, pos0=7999)):
+        p2 = _pdesc(**{**dict(batch=2, n_cells=8192, pos0=8191, Hkv=2, D=256, d_idx=128),
+                       **bad})
+        assert _step_call(p2, idsc, ad) == INVALID, bad
+    # T must agree across the three descriptors
+    p2 = _pdesc(batch=2, T=2, n_cells=8192, pos0=8190, Hkv=2, D=256, d_idx=128)
+    assert _step_call(p2, idsc, ad) == INVALID
+    assert _step_call(pd, _idesc(batch=2, n_cells=8192, pos0=8191, ids_cap=2100), ad) == INVALID
+    assert _step_call(pd, idsc, _adesc(batch=2, n_cells=8192, T=2)) == INVALID
+    assert _step_call(pd, idsc, _adesc(batch=2, n_cells=8192,
+                                       strides=dict(kq_cell_stride=1024))) == INVALID
+    p64 = _pdesc(batch=2, n_cells=8192, pos0=8191, Hkv=2, D=256, d_idx=64)
+    assert _step_call(p64, idsc, ad) == INVALID
+    assert _step_call(pd, idsc, _adesc(batch=2, n_cells=8192, P=65)) == UNSUPPORTED
+    need = qb.lib().qsa_step_workspace(ctypes.byref(idsc), ctypes.byref(ad))
+    assert _step_call(pd, idsc, ad, ws=None) == WORKSPACE
+    assert _step_call(pd, idsc, ad, ws_bytes=need - 1) == WORKSPACE
+    assert _step_call(pd, idsc, ad, ws=16) == WORKSPACE               # not 256-byte aligned
+    assert _step_call(pd, idsc, ad, gate=8) == INVALID
 
 
 def test_probe_library_exports():

@@ -8,6 +8,7 @@ from .qsa import (QSA_ATTEND_AUTO, QSA_ATTEND_MATRIX, QSA_ATTEND_VECTOR,  # noqa
                   QSA_F16, QSA_F32, QSA_NOALLOC_WORKSPACE_BYTES,  # noqa: F401
                   AppendDesc, AttnDesc, IndexDesc, QsaError,  # noqa: F401
                   QsaPath, append_desc, attn_desc, index_desc, path_for, qsa_attend,
+                  qsa_attend_merge, qsa_step, qsa_step_workspace, StepCall,
                   qsa_decode_window, qsa_decode_window_workspace,
                   qsa_index_topk, qsa_index_topk_noalloc, qsa_kv_append, qsa_merge_gated,
                   qsa_index_topk_workspace, qsa_merge, qsa_partials_floats, to_device)

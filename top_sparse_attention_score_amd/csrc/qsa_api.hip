@@ -220,6 +220,44 @@ size_t partial_rows(const qsa_attn_desc* d)
     return (size_t)d->batch * (size_t)d->T * (size_t)d->Hq * (size_t)d->P;
 }
 
+// The three descriptors of one step describe the same problems: equal T,
+// batch and n_cells, the append's cells are the index tokens' positions,
+// equal Hkv, D and ids_cap, equal d_idx when index keys are appended, and
+// the same resolved cache strides.
+bool same_step(const qsa_append_desc* pd, const qsa_index_desc* id, const qsa_attn_desc* ad,
+               const qsa::AppendLaunch& ap, const qsa::AttnLaunch& at, bool with_kidx)
+{
+    if (pd->T != id->T || ad->T != id->T || pd->batch != id->batch || ad->batch != id->batch ||
+        pd->n_cells != id->n_cells || ad->n_cells != id->n_cells || pd->pos0 != id->pos0 ||
+        pd->Hkv != ad->Hkv || pd->D != ad->D || ad->ids_cap != id->ids_cap ||
+        (with_kidx && pd->d_idx != id->d_idx))
+        return false;
+    return ap.kq_cs == at.kq_cs && ap.ksc_cs == at.ksc_cs && ap.vq_cs == at.vq_cs &&
+           ap.vsc_cs == at.vsc_cs && ap.kq_bs == at.kq_bs && ap.ksc_bs == at.ksc_bs &&
+           ap.vq_bs == at.vq_bs && ap.vsc_bs == at.vsc_bs;
+}
+
+// The attention and the merge run as one kernel (qsa_attend_merge).
+bool merge_fuses(const qsa::AttnLaunch& at)
+{
+    return at.algo != QSA_ATTEND_VECTOR && (at.P == 1 || at.P == 2 || at.P == 4);
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of qsa_step: the index workspace, then (when the merge is a
+// separate kernel) the partials, 256-byte aligned.
+size_t step_workspace_bytes(const qsa_index_desc* id, const qsa_attn_desc* ad,
+                            const qsa::AttnLaunch& at)
+{
+    size_t n = round_up(qsa::index_workspace_bytes(id->batch, id->T, id->n_cells), 256);
+    if (!merge_fuses(at)) {
+        const size_t rows = partial_rows(ad);
+        n += round_up((2 * rows + rows * (size_t)ad->D) * sizeof(float), 256);
+    }
+    return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,6 +386,39 @@ int qsa_merge(const qsa_attn_desc* desc, const float* partials, void* out, void*
     return qsa_merge_gated(desc, partials, nullptr, out, stream);
 }
 
+int qsa_attend_merge(const qsa_attn_desc* desc, const void* q, const int8_t* Kq, const void* Ksc,
+                     const int8_t* Vq, const void* Vsc, const int32_t* ids, const int32_t* n_sel,
+                     const void* gate, void* out, void* stream)
+{
+    qsa::AttnLaunch a;
+    const int st = check_attn(desc, &a);
+    if (st != QSA_OK)
+        return st;
+    if (!q || !Kq || !Ksc || !Vq || !Vsc || !ids || !n_sel || !out)
+        return QSA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(Kq, 16) || !aligned(Ksc, 16) || !aligned(Vq, 16) ||
+        !aligned(Vsc, 16) || !aligned(ids, 4) || !aligned(n_sel, 4) || !aligned(out, 16) ||
+        (gate && !aligned(gate, 16)))
+        return QSA_ERR_INVALID_ARG;
+    // One workgroup holds four (token, chunk) items: the chunks of a token
+    // must fit one workgroup.
+    if (a.algo == QSA_ATTEND_VECTOR || (a.P != 1 && a.P != 2 && a.P != 4))
+        return QSA_ERR_UNSUPPORTED;
+    a.q = q;
+    a.Kq = Kq;
+    a.Ksc = Ksc;
+    a.Vq = Vq;
+    a.Vsc = Vsc;
+    a.ids = ids;
+    a.n_sel = n_sel;
+    a.pm = a.pl = a.po = nullptr;
+    a.out = out;
+    a.gate = gate;
+    if (qsa::launch_attend(a, (hipStream_t)stream) != hipSuccess)
+        return QSA_ERR_HIP;
+    return QSA_OK;
+}
+
 int qsa_kv_append(const qsa_append_desc* d, const float* k_new, const float* v_new,
                   const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc,
                   void* K_idx, void* stream)
@@ -388,15 +459,7 @@ int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc* idesc,
     if (st != QSA_OK)
         return st;
     // One step of the same problems, read from the cache the append writes.
-    if (pdesc->T != 1 || idesc->T != 1 || adesc->T != 1 || pdesc->batch != idesc->batch ||
-        adesc->batch != idesc->batch || pdesc->n_cells != idesc->n_cells ||
-        adesc->n_cells != idesc->n_cells || pdesc->pos0 != idesc->pos0 ||
-        pdesc->Hkv != adesc->Hkv || pdesc->D != adesc->D || adesc->ids_cap != idesc->ids_cap ||
-        (kidx_new && pdesc->d_idx != idesc->d_idx))
-        return QSA_ERR_INVALID_ARG;
-    if (ap.kq_cs != at.kq_cs || ap.ksc_cs != at.ksc_cs || ap.vq_cs != at.vq_cs ||
-        ap.vsc_cs != at.vsc_cs || ap.kq_bs != at.kq_bs || ap.ksc_bs != at.ksc_bs ||
-        ap.vq_bs != at.vq_bs || ap.vsc_bs != at.vsc_bs)
+    if (pdesc->T != 1 || !same_step(pdesc, idesc, adesc, ap, at, kidx_new != nullptr))
         return QSA_ERR_INVALID_ARG;
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16) || (gate && !aligned(gate, 16)) ||
         !aligned(Ksc, 16) || !aligned(Vsc, 16))
@@ -418,6 +481,73 @@ int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc* idesc,
     at.out = out;
     at.gate = gate;
     if (qsa::launch_window(ap, ix, at, ws, (hipStream_t)stream) != hipSuccess)
+        return QSA_ERR_HIP;
+    return QSA_OK;
+}
+
+size_t qsa_step_workspace(const qsa_index_desc* idesc, const qsa_attn_desc* adesc)
+{
+    qsa::AttnLaunch at;
+    if (check_index(idesc) != QSA_OK || check_attn(adesc, &at) != QSA_OK)
+        return 0;
+    return step_workspace_bytes(idesc, adesc, at);
+}
+
+int qsa_step(const qsa_append_desc* pdesc, const qsa_index_desc* idesc,
+             const qsa_attn_desc* adesc, const float* k_new, const float* v_new,
+             const float* kidx_new, int8_t* Kq, void* Ksc, int8_t* Vq, void* Vsc, void* K_idx,
+             const void* q_idx, const void* q, const void* gate, int32_t* ids, int32_t* n_sel,
+             void* out, void* ws, size_t ws_bytes, void* stream)
+{
+    qsa::AppendLaunch ap;
+    qsa::IndexLaunch ix;
+    qsa::AttnLaunch at;
+    int st = fill_append(pdesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, &ap);
+    if (st == QSA_OK)
+        st = fill_index(idesc, q_idx, K_idx, ids, n_sel, &ix);
+    if (st == QSA_OK)
+        st = check_attn(adesc, &at);
+    if (st != QSA_OK)
+        return st;
+    if (!same_step(pdesc, idesc, adesc, ap, at, kidx_new != nullptr))
+        return QSA_ERR_INVALID_ARG;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16) || (gate && !aligned(gate, 16)) ||
+        !aligned(Ksc, 16) || !aligned(Vsc, 16))
+        return QSA_ERR_INVALID_ARG;
+    const size_t need = step_workspace_bytes(idesc, adesc, at);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return QSA_ERR_WORKSPACE;
+    ix.ws = ws;
+    at.q = q;
+    at.Kq = Kq;
+    at.Ksc = Ksc;
+    at.Vq = Vq;
+    at.Vsc = Vsc;
+    at.ids = ids;
+    at.n_sel = n_sel;
+    at.out = out;
+    at.gate = gate;
+    const hipStream_t s = (hipStream_t)stream;
+    if (qsa::launch_index_topk(ix, s, &ap) != hipSuccess)
+        return QSA_ERR_HIP;
+    if (merge_fuses(at)) {
+        at.pm = at.pl = at.po = nullptr;
+        if (qsa::launch_attend(at, s) != hipSuccess)
+            return QSA_ERR_HIP;
+        return QSA_OK;
+    }
+    const size_t rows = partial_rows(adesc);
+    float* part = (float*)((char*)ws + round_up(
+        qsa::index_workspace_bytes(idesc->batch, idesc->T, idesc->n_cells), 256));
+    at.pm = part;
+    at.pl = part + rows;
+    at.po = part + 2 * rows;
+    void* out_keep = at.out;
+    at.out = nullptr;  // qsa_attend writes the partials
+    if (qsa::launch_attend(at, s) != hipSuccess)
+        return QSA_ERR_HIP;
+    at.out = out_keep;
+    if (qsa::launch_merge(at, s) != hipSuccess)
         return QSA_ERR_HIP;
     return QSA_OK;
 }

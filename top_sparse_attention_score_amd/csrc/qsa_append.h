@@ -57,17 +57,85 @@ __device__ __forceinline__ uint16_t scale_bits(float a)
     return best;
 }
 
-// Items: 8 lanes per 32-element block of K or V (4 elements each; the
-// block maximum is combined over the 8 consecutive lanes), then one lane per
-// 4 index-key elements.  Blocks occupy whole 8-lane groups, so the shuffles
-// stay inside a group.
+// Lane w of the quantisation items: 8 lanes per 32-element block of K or
+// V (4 elements each; the block maximum is combined over the 8 consecutive
+// lanes, so all 8 lanes of a group must call this together; `live` false
+// makes a lane take part in the shuffles only).
+// w = ((((b * T + t) * Hkv + g) * NB + sb32) * 2 + which) * 8 + sub
+__device__ __forceinline__ void append_quant_lane(const AppendLaunch& a, long long w, bool live)
+{
+    const int NB = a.D / 32;
+    const int sub = (int)(w & 7);
+    long long r = w >> 3;
+    const int which = (int)(r & 1);
+    r >>= 1;
+    const int sb32 = (int)(r % NB);  // 32-element block of the row
+    r /= NB;
+    const int g = (int)(r % a.Hkv);
+    r /= a.Hkv;
+    const int t = (int)(r % a.T);
+    const int b = (int)(r / a.T);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+        const float* src = (which ? a.v_new : a.k_new) +
+                           (((size_t)b * a.T + t) * a.Hkv + g) * a.D + 32 * sb32 + 4 * sub;
+        v = *(const float4*)src;
+    }
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+    if (!live)
+        return;
+    const uint16_t sb = scale_bits(amax);
+    const double s = (double)half_bits_to_float(sb);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        int c = 0;
+        if (s > 0.0) {
+            const double qv = rint((double)x[e] / s);
+            c = (int)fmin(fmax(qv, -127.0), 127.0);
+        }
+        word |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * e);
+    }
+    const long long cell = (long long)(a.pos0 + t);
+    int8_t* codes = (which ? a.Vq : a.Kq) + (long long)b * (which ? a.vq_bs : a.kq_bs) +
+                    cell * (which ? a.vq_cs : a.kq_cs) + (long long)g * a.D + 32 * sb32 + 4 * sub;
+    *(uint32_t*)codes = word;
+    if (sub == 0) {
+        char* sc = (char*)(which ? a.Vsc : a.Ksc) + (long long)b * (which ? a.vsc_bs : a.ksc_bs) +
+                   cell * (which ? a.vsc_cs : a.ksc_cs) + ((long long)g * NB + sb32) * 2;
+        *(uint16_t*)sc = sb;
+    }
+}
+
+// Lane r of the index-key items: 4 elements of (b, t), r = (b * T + t) *
+// (DI / 4) + i.
+__device__ __forceinline__ void append_index_lane(const AppendLaunch& a, long long r)
+{
+    const int per = a.DI / 4;
+    const int i = (int)(r % per);
+    const long long bt = r / per;
+    const int t = (int)(bt % a.T);
+    const int b = (int)(bt / a.T);
+    const float4 v = ((const float4*)(a.kidx_new + (size_t)bt * a.DI))[i];
+    const uint16_t h0 = f16_bits((_Float16)v.x), h1 = f16_bits((_Float16)v.y);
+    const uint16_t h2 = f16_bits((_Float16)v.z), h3 = f16_bits((_Float16)v.w);
+    uint16_t* dst = a.K_idx + ((size_t)b * a.N + a.pos0 + t) * a.DI + 4 * i;
+    ((uint2*)dst)[0] = make_uint2((uint32_t)h0 | ((uint32_t)h1 << 16),
+                                  (uint32_t)h2 | ((uint32_t)h3 << 16));
+}
+
+// Items: the quantisation lanes, then one lane per 4 index-key elements.
+// Blocks occupy whole 8-lane groups, so the shuffles stay inside a group.
 // Workgroup blk of nblk (256 threads each) takes every nblk-th group of 256
 // items.
 __device__ __forceinline__ void append_blocks(const AppendLaunch& a, long long q_lanes,
                                               long long n_quant, long long n_idx, int blk,
                                               int nblk)
 {
-    const int NB = a.D / 32;
     const long long total = n_quant + n_idx;  // n_quant: q_lanes rounded up to 256
     const long long stride = (long long)nblk * 256;
     for (long long w0 = (long long)blk * 256; w0 < total; w0 += stride) {
@@ -75,70 +143,27 @@ __device__ __forceinline__ void append_blocks(const AppendLaunch& a, long long q
         if (w0 < n_quant) {
             // The whole workgroup is in the quantisation range (n_quant is a
             // multiple of 256), so every lane reaches the shuffles.
-            // w = ((((b * T + t) * Hkv + g) * NB + sb32) * 2 + which) * 8 + sub
-            const int sub = (int)(w & 7);
-            long long r = w >> 3;
-            const int which = (int)(r & 1);
-            r >>= 1;
-            const int sb32 = (int)(r % NB);  // 32-element block of the row
-            r /= NB;
-            const int g = (int)(r % a.Hkv);
-            r /= a.Hkv;
-            const int t = (int)(r % a.T);
-            const int b = (int)(r / a.T);
-            const bool live = w < q_lanes;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live) {
-                const float* src = (which ? a.v_new : a.k_new) +
-                                   (((size_t)b * a.T + t) * a.Hkv + g) * a.D + 32 * sb32 + 4 * sub;
-                v = *(const float4*)src;
-            }
-            float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-            for (int o = 1; o < 8; o <<= 1)
-                amax = fmaxf(amax, __shfl_xor(amax, o, 8));
-            if (!live)
-                continue;
-            const uint16_t sb = scale_bits(amax);
-            const double s = (double)half_bits_to_float(sb);
-            const float x[4] = {v.x, v.y, v.z, v.w};
-            uint32_t word = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                int c = 0;
-                if (s > 0.0) {
-                    const double qv = rint((double)x[e] / s);
-                    c = (int)fmin(fmax(qv, -127.0), 127.0);
-                }
-                word |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * e);
-            }
-            const long long cell = (long long)(a.pos0 + t);
-            int8_t* codes = (which ? a.Vq : a.Kq) + (long long)b * (which ? a.vq_bs : a.kq_bs) +
-                            cell * (which ? a.vq_cs : a.kq_cs) + (long long)g * a.D + 32 * sb32 +
-                            4 * sub;
-            *(uint32_t*)codes = word;
-            if (sub == 0) {
-                char* sc = (char*)(which ? a.Vsc : a.Ksc) +
-                           (long long)b * (which ? a.vsc_bs : a.ksc_bs) +
-                           cell * (which ? a.vsc_cs : a.ksc_cs) + ((long long)g * NB + sb32) * 2;
-                *(uint16_t*)sc = sb;
-            }
+            append_quant_lane(a, w, w < q_lanes);
         } else if (w < total) {
-            // index keys: 4 elements of (b, t) (n_quant is a multiple of 256,
-            // so this whole workgroup is in the index range)
-            const long long r = w - n_quant;
-            const int per = a.DI / 4;
-            const int i = (int)(r % per);
-            const long long bt = r / per;
-            const int t = (int)(bt % a.T);
-            const int b = (int)(bt / a.T);
-            const float4 v = ((const float4*)(a.kidx_new + (size_t)bt * a.DI))[i];
-            const uint16_t h0 = f16_bits((_Float16)v.x), h1 = f16_bits((_Float16)v.y);
-            const uint16_t h2 = f16_bits((_Float16)v.z), h3 = f16_bits((_Float16)v.w);
-            uint16_t* dst = a.K_idx + ((size_t)b * a.N + a.pos0 + t) * a.DI + 4 * i;
-            ((uint2*)dst)[0] = make_uint2((uint32_t)h0 | ((uint32_t)h1 << 16),
-                                          (uint32_t)h2 | ((uint32_t)h3 << 16));
+            // index keys (n_quant is a multiple of 256, so this whole
+            // workgroup is in the index range)
+            append_index_lane(a, w - n_quant);
         }
+    }
+}
+
+// The items of problem b only, by the `nthreads` threads of one workgroup
+// (a multiple of 8): its T tokens' K and V blocks, then their index keys
+// (when kidx_new is given).
+__device__ __forceinline__ void append_problem(const AppendLaunch& a, int b, int nthreads)
+{
+    const long long nq = (long long)a.T * a.Hkv * (a.D / 32) * 16;  // a multiple of 16
+    for (long long l = threadIdx.x; l < nq; l += nthreads)
+        append_quant_lane(a, (long long)b * nq + l, true);
+    if (a.kidx_new) {
+        const long long ni = (long long)a.T * (a.DI / 4);
+        for (long long l = threadIdx.x; l < ni; l += nthreads)
+            append_index_lane(a, (long long)b * ni + l);
     }
 }
 

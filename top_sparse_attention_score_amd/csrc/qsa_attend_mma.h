@@ -64,6 +64,7 @@
 #include <math.h>
 
 #include "qsa_device.h"
+#include "qsa_merge.h"
 #include "qsa_mma.h"
 
 namespace qsa {
@@ -75,7 +76,17 @@ constexpr int kMmaWaves = 4;      // (token, chunk) items per workgroup
 // split query through LDS (requires P % 4 == 0).  With the query in LDS, or
 // fp16 queries (no lo half) in registers, the kernel fits 256 registers and
 // runs two waves per SIMD; fp32 queries in registers need one wave per SIMD.
-template <int G, int D, bool QF16, bool SHQ>
+//
+// MERGE: the workgroup's four items are all the chunks of whole tokens (P in
+// {1, 2, 4}), so instead of writing partials the workgroup merges them
+// itself (with the optional output gate) and writes the output: each wave
+// leaves m and l in its weight table and its o, scaled exactly as the
+// partial would be, in LDS (the V tiles' space, a few heads per round), and
+// the merge runs the sequence of the merge kernel on those values, so the
+// output equals qsa_attend followed by qsa_merge(_gated) bit for bit.
+// Every wave, also one with an empty chunk or past the last item, takes
+// part in the workgroup barriers of that epilogue.
+template <int G, int D, bool QF16, bool SHQ, bool MERGE = false>
 __device__ __forceinline__ void attend_mma_block(
     int wg, const void* __restrict__ q, const int8_t* __restrict__ Kq,
     const uint8_t* __restrict__ Ksc, const int8_t* __restrict__ Vq,
@@ -83,7 +94,8 @@ __device__ __forceinline__ void attend_mma_block(
     long long vsc_cs, long long kq_bs, long long ksc_bs, long long vq_bs, long long vsc_bs,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ n_sel, float* __restrict__ pm,
     float* __restrict__ pl, float* __restrict__ po, int T, int Hq, int Hkv, int P, int cap, int N,
-    int BT, float scale)
+    int BT, float scale, void* __restrict__ out = nullptr, const void* __restrict__ gate = nullptr,
+    int out_f16 = 0)
 {
     static_assert(G <= 16, "one 16-row head block per KV head");
     constexpr int NB = D / 32;                // scale blocks per head row
@@ -99,6 +111,12 @@ __device__ __forceinline__ void attend_mma_block(
     __shared__ __align__(16) float p_all[kMmaWaves][16 * PP];
     __shared__ __align__(16) half8_t q_all[SHQ ? QH * NB * 64 : 1];
     __shared__ float s_qmax[kMmaWaves];
+    // MERGE with a gate: the gate rows of the workgroup's tokens (G heads of
+    // D elements each, in the query dtype), copied at the start.
+    constexpr int GTOK = SHQ ? 1 : kMmaWaves;   // tokens per workgroup, at most
+    constexpr int GES = QF16 ? 2 : 4;           // gate element bytes
+    constexpr int GBYTES = GTOK * G * D * GES;
+    __shared__ __align__(16) uint8_t gate_s[MERGE ? (GBYTES + 1023) / 1024 * 1024 : 16];
 
     // Workgroup w serves KV head g = (w / 8) % Hkv of item group
     // (w / (8 Hkv)) * 8 + w % 8: the groups' KV heads are 8 workgroup ids
@@ -114,6 +132,28 @@ __device__ __forceinline__ void attend_mma_block(
     const int hq = lane & 15, q4 = lane >> 4;
     if (group * kMmaWaves >= (long long)BT * P)
         return;  // grid padding (whole workgroup)
+
+    if constexpr (MERGE) {
+        // Gate rows of this workgroup's tokens into LDS, 16 bytes a lane,
+        // by direct copies that complete during the first tile (every wave
+        // waits for them before the epilogue reads them).
+        if (gate) {
+            constexpr int UPT = G * D * GES / 16;  // 16-byte units per token
+            const long long bt0 = group * kMmaWaves / P;
+            const int ntok = (int)min((long long)(kMmaWaves / P), (long long)BT - bt0);
+            const int units = ntok * UPT;
+            for (int u0 = wave * 64; u0 < units; u0 += 64 * kMmaWaves) {
+                const int u = u0 + lane;
+                if (u < units) {
+                    const int tl = u / UPT, w = u % UPT;
+                    const char* src = (const char*)gate +
+                                      (((bt0 + tl) * Hq + (long long)g * G) * D) * GES + 16 * w;
+                    __builtin_amdgcn_global_load_lds((const void*)src,
+                                                     (lds_void_t*)(gate_s + 16 * u0), 16, 0, 0);
+                }
+            }
+        }
+    }
 
     int eq = 0;  // fp32 queries are split as q * 2^-eq (see the header)
     if constexpr (SHQ) {
@@ -141,21 +181,24 @@ __device__ __forceinline__ void attend_mma_block(
         }
         __syncthreads();
     }
-    if (item >= (long long)BT * P)
-        return;
-    const int bt = (int)(item / P), c = (int)(item % P);
+    const bool live = item < (long long)BT * P;
+    if constexpr (!MERGE) {
+        if (!live)
+            return;
+    }
+    const int bt = live ? (int)(item / P) : 0, c = live ? (int)(item % P) : 0;
     int8_t* v_s = v_all[wave];
     uint32_t* vsc_s = vsc_all[wave];
     float* p_s = p_all[wave];
     const int b = bt / T;
     const size_t prow = (size_t)bt * Hq + (size_t)g * G;  // row of head g*G
 
-    const int ns = min(n_sel[bt], cap);
+    const int ns = live ? min(n_sel[bt], cap) : 0;
     const int S = (ns + P - 1) / P;
     const int beg = c * S;
     const int end = min(beg + S, ns);
 
-    if (beg >= end) {
+    if (!MERGE && beg >= end) {
         if (lane < G) {
             pm[(prow + lane) * P + c] = -INFINITY;
             pl[(prow + lane) * P + c] = 0.f;
@@ -167,6 +210,20 @@ __device__ __forceinline__ void attend_mma_block(
         return;
     }
 
+    float m_run[4], m_ref[4], l_run[4];  // heads 4*q4 + r
+    float4_t o[NT];                      // O^T: head hq, elements 16*t + 4*q4 + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m_run[r] = -INFINITY;
+        m_ref[r] = -INFINITY;
+        l_run[r] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        o[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+    int ev = 0;  // the accumulated output carries 2^ev (see the header)
+
+    if (beg < end) {  // always true here without MERGE
     half8_t qh[SHQ ? 1 : NB], ql[SHQ ? 1 : NB];
     if constexpr (!SHQ) {
         if constexpr (!QF16) {
@@ -224,18 +281,6 @@ __device__ __forceinline__ void attend_mma_block(
         }
     };
 
-    float m_run[4], m_ref[4], l_run[4];  // heads 4*q4 + r
-    float4_t o[NT];                      // O^T: head hq, elements 16*t + 4*q4 + r
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m_run[r] = -INFINITY;
-        m_ref[r] = -INFINITY;
-        l_run[r] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-        o[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-
     int t0 = beg;
     int nt = min(TC, end - t0);
     int jv, ja, jb;
@@ -246,7 +291,6 @@ __device__ __forceinline__ void attend_mma_block(
     // Transpose-read base of this lane: cell 8*q4 + hq/2 of the [chunk][cell]
     // table, 8-byte half hq&1; slice t adds 512*t.
     const int8_t* v_rd = v_s + 16 * (8 * q4 + (hq >> 1)) + 8 * (hq & 1);
-    int ev = 0;  // the accumulated output carries 2^ev (see the header)
 
 #pragma unroll 1
     for (;;) {
@@ -414,27 +458,105 @@ __device__ __forceinline__ void attend_mma_block(
         jv = jvn;
     }
 
-    // ---- partials: m, and l, o brought from the reference max to m ---------
+    }  // beg < end
+
+    if constexpr (!MERGE) {
+        // ---- partials: m, and l, o brought from the reference max to m -----
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = 4 * q4 + r;
-        const float f = __builtin_amdgcn_exp2f((m_ref[r] - m_run[r]) * kLog2e);
-        if (hq == 0) {
-            p_s[h * PP + 33] = f;
-            if (h < G) {
-                pm[(prow + h) * P + c] = m_run[r];
-                pl[(prow + h) * P + c] = l_run[r] * f;
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * q4 + r;
+            const float f = __builtin_amdgcn_exp2f((m_ref[r] - m_run[r]) * kLog2e);
+            if (hq == 0) {
+                p_s[h * PP + 33] = f;
+                if (h < G) {
+                    pm[(prow + h) * P + c] = m_run[r];
+                    pl[(prow + h) * P + c] = l_run[r] * f;
+                }
             }
         }
-    }
-    wave_lds_sync();
-    if (hq < G) {
-        const float f = __builtin_amdgcn_ldexpf(p_s[hq * PP + 33] * (1.f / kWScale), -ev);
-        float* dst = po + ((prow + hq) * P + c) * D + 4 * q4;
+        wave_lds_sync();
+        if (hq < G) {
+            const float f = __builtin_amdgcn_ldexpf(p_s[hq * PP + 33] * (1.f / kWScale), -ev);
+            float* dst = po + ((prow + hq) * P + c) * D + 4 * q4;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float4_t v = o[t] * f;
-            *(float4*)(dst + 16 * t) = make_float4(v[0], v[1], v[2], v[3]);
+            for (int t = 0; t < NT; ++t) {
+                const float4_t v = o[t] * f;
+                *(float4*)(dst + 16 * t) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    } else {
+        // ---- fused merge: the same partial values, merged in LDS ------------
+        // m and l of head h at slots 34 and 35 of row h of the wave's weight
+        // table; o (scaled as the partial) stays in registers until staged.
+        if (beg < end) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = 4 * q4 + r;
+                const float f = __builtin_amdgcn_exp2f((m_ref[r] - m_run[r]) * kLog2e);
+                if (hq == 0) {
+                    p_s[h * PP + 33] = f;
+                    p_s[h * PP + 34] = m_run[r];
+                    p_s[h * PP + 35] = l_run[r] * f;
+                }
+            }
+            wave_lds_sync();
+            const float f = __builtin_amdgcn_ldexpf(p_s[hq * PP + 33] * (1.f / kWScale), -ev);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                o[t] = o[t] * f;
+        } else {  // empty chunk or no item: m = -inf, l = 0, o = 0
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (hq == 0) {
+                    p_s[(4 * q4 + r) * PP + 34] = -INFINITY;
+                    p_s[(4 * q4 + r) * PP + 35] = 0.f;
+                }
+            }
+        }
+        // Stage: [wave][head of the round][D + 4] floats over the V tiles
+        // (the pad spreads a wave's 16 head rows over the LDS banks).
+        constexpr int SP = D + 4;
+        constexpr int HR = (int)(sizeof(v_all) / (kMmaWaves * SP * sizeof(float)));
+        static_assert(HR >= 1, "stage holds at least one head per round");
+        float* stage = (float*)&v_all[0][0];
+        const int ntok = kMmaWaves / P;                    // tokens of this workgroup
+        const long long bt0 = group * kMmaWaves / P;       // its first token
+        // Every wave is out of its tile loop (the V tiles are free) and its
+        // gate copies have landed.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+#pragma unroll 1
+        for (int h0 = 0; h0 < G; h0 += HR) {
+            const int hr = min(HR, G - h0);
+            if (hq >= h0 && hq < h0 + hr) {
+                float* dst = stage + (wave * HR + (hq - h0)) * SP + 4 * q4;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    *(float4_t*)(dst + 16 * t) = o[t];
+            }
+            __syncthreads();
+            const int n4 = ntok * hr * (D / 4);
+            for (int i = threadIdx.x; i < n4; i += 64 * kMmaWaves) {
+                const int d4 = i % (D / 4);
+                const int hl = (i / (D / 4)) % hr;
+                const int tl = i / ((D / 4) * hr);
+                const long long tok = bt0 + tl;
+                if (tok >= BT)
+                    continue;
+                const int h = h0 + hl;
+                const int w0 = tl * P;  // wave of chunk 0 of this token
+                float res[4];
+                merge_elems<4>(&p_all[w0][h * PP + 34], &p_all[w0][h * PP + 35], 16 * PP,
+                               stage + (w0 * HR + hl) * SP + 4 * d4, (long long)HR * SP, P, res);
+                const long long off = (tok * Hq + (long long)g * G + h) * D + 4 * d4;
+                const void* gs = gate ? (const void*)gate_s : nullptr;
+                const long long goff = ((long long)tl * G + h) * D + 4 * d4;
+                if (out_f16)
+                    gate_store<4, true>(res, gs, QF16 ? 1 : 0, goff, out, off);
+                else
+                    gate_store<4, false>(res, gs, QF16 ? 1 : 0, goff, out, off);
+            }
+            __syncthreads();  // stage read before the next round overwrites it
         }
     }
 }

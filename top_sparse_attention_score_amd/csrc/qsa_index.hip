@@ -37,6 +37,7 @@
 //                the whole chip (histogram, filter + pivot, ordered write).
 #include <algorithm>
 
+#include "qsa_append.h"
 #include "qsa_device.h"
 #include "qsa_launch.h"
 #include "qsa_select.h"
@@ -810,13 +811,22 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_row(const uint32_t* __restr
 // threads score the visible key rows (16 lanes per 256-byte row as in
 // k_idx_scan, eight rows in flight per lane) into an LDS key table, then
 // select from it.  Used while the row's keys fit in LDS.
-template <int DI, int KPT>
+// APPEND: the workgroup first writes its problem's new token into the cache
+// (the lanes qsa_kv_append runs for that problem), so the scan below reads
+// the new cell's index key; the barrier orders the writes before the reads
+// (one workgroup, one CU).
+template <int DI, int KPT, bool APPEND>
 __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __restrict__ q_idx,
                                                              const uint4* __restrict__ K_idx,
                                                              int32_t* __restrict__ ids,
                                                              int32_t* __restrict__ n_sel, int N,
-                                                             int pos0, int k, int dense_max, int cap)
+                                                             int pos0, int k, int dense_max, int cap,
+                                                             AppendLaunch ap)
 {
+    if constexpr (APPEND) {
+        append_problem(ap, blockIdx.x, kRowThreads);
+        __syncthreads();
+    }
     constexpr int LPR = DI / 8;                // lanes per key row
     constexpr int RPS = kRowThreads / LPR;     // rows per block-wide step
     constexpr int U = 16;                      // steps in flight per thread
@@ -1571,7 +1581,7 @@ static void launch_gemm(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipS
                                          keys, a.T, a.N, nvis_max);
 }
 
-hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
+hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLaunch* ap)
 {
     SelWs w = carve(a.ws, a.B, a.T, a.N, nullptr);
     const int BT = a.B * a.T;
@@ -1584,9 +1594,16 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
     if (any_select && a.T == 1 && a.N <= kRowThreads * 16 && a.B >= 128) {
         const uint4* q = (const uint4*)a.q_idx;
         const uint4* K = (const uint4*)a.K_idx;
-#define QSA_FUSED(DI, KPT)                                                               \
-    k_scan_select<DI, KPT><<<a.B, kRowThreads, 0, s>>>(q, K, a.ids, a.n_sel, a.N, a.pos0, a.k, \
-                                                       a.dense_max, a.cap)
+        const AppendLaunch none{};
+#define QSA_FUSED(DI, KPT)                                                                      \
+    do {                                                                                        \
+        if (ap)                                                                                 \
+            k_scan_select<DI, KPT, true><<<a.B, kRowThreads, 0, s>>>(                           \
+                q, K, a.ids, a.n_sel, a.N, a.pos0, a.k, a.dense_max, a.cap, *ap);               \
+        else                                                                                    \
+            k_scan_select<DI, KPT, false><<<a.B, kRowThreads, 0, s>>>(                          \
+                q, K, a.ids, a.n_sel, a.N, a.pos0, a.k, a.dense_max, a.cap, none);              \
+    } while (0)
         const int kpt = row_select_kpt(a.N);
         if (a.DI == 64) {
             if (kpt <= 4) QSA_FUSED(64, 4); else if (kpt <= 8) QSA_FUSED(64, 8); else QSA_FUSED(64, 16);
@@ -1595,6 +1612,12 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s)
         }
 #undef QSA_FUSED
         return hipGetLastError();
+    }
+    // Every other path: the append as its own kernel first.
+    if (ap) {
+        const hipError_t e = launch_kv_append(*ap, s);
+        if (e != hipSuccess)
+            return e;
     }
     const bool fused = any_select && a.T > 16 && a.N <= kFusedMaxCells &&
                        nvis_max >= kFusedMinCells && a.k <= kCandCap / 2;

@@ -24,7 +24,14 @@ size_t index_workspace_bytes(int B, int T, int N);
 // Largest n_cells the select kernels handle.
 int index_max_cells();
 
-hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s);
+struct AttnLaunch;
+struct AppendLaunch;
+
+// With `ap` (the same step's append: T == a.T, pos0 == a.pos0, same B and
+// N) the new tokens are written into the cache first: inside the scan
+// kernel where one workgroup serves one problem, else by the append kernel.
+hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s,
+                             const AppendLaunch* ap = nullptr);
 
 struct AttnLaunch {
     int B, T, Hq, Hkv, D, P, cap, N;
@@ -68,6 +75,8 @@ hipError_t launch_kv_append(const AppendLaunch& a, hipStream_t s);
 
 hipError_t launch_attend(const AttnLaunch& a, hipStream_t s);
 // Matrix-core attend kernel (qsa_attend_mma.hip); false if no variant fits.
+// With a.out set (P in {1, 2, 4}) the kernel also merges the chunks, applies
+// a.gate and writes a.out instead of the partials.
 bool launch_attend_mma(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_merge(const AttnLaunch& a, hipStream_t s);
 

@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_merge.restype = _c_int
         L.qsa_merge_gated.argtypes = [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp]
         L.qsa_merge_gated.restype = _c_int
+        L.qsa_attend_merge.argtypes = [ctypes.POINTER(AttnDesc)] + [_vp] * 10
+        L.qsa_attend_merge.restype = _c_int
         L.qsa_kv_append.argtypes = [ctypes.POINTER(AppendDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp]
         L.qsa_kv_append.restype = _c_int
@@ -97,6 +99,11 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(AttnDesc)] + [_vp] * 15 + \
                                        [ctypes.c_size_t, _vp]
         L.qsa_decode_window.restype = _c_int
+        L.qsa_step_workspace.argtypes = [ctypes.POINTER(IndexDesc), ctypes.POINTER(AttnDesc)]
+        L.qsa_step_workspace.restype = ctypes.c_size_t
+        L.qsa_step.argtypes = [ctypes.POINTER(AppendDesc), ctypes.POINTER(IndexDesc),
+                               ctypes.POINTER(AttnDesc)] + [_vp] * 15 + [ctypes.c_size_t, _vp]
+        L.qsa_step.restype = _c_int
         _lib = L
     return _lib
 
@@ -190,6 +197,13 @@ def qsa_merge_gated(desc: AttnDesc, partials, gate, out, stream=None) -> None:
                                  _stream(stream)), "qsa_merge_gated")
 
 
+def qsa_attend_merge(desc: AttnDesc, q, Kq, Ksc, Vq, Vsc, ids, n_sel, gate, out,
+                     stream=None) -> None:
+    _check(lib().qsa_attend_merge(ctypes.byref(desc), _ptr(q), _ptr(Kq), _ptr(Ksc), _ptr(Vq),
+                                  _ptr(Vsc), _ptr(ids), _ptr(n_sel), _ptr(gate), _ptr(out),
+                                  _stream(stream)), "qsa_attend_merge")
+
+
 def qsa_kv_append(desc: AppendDesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
                   stream=None) -> None:
     _check(lib().qsa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(kidx_new),
@@ -210,6 +224,41 @@ def qsa_decode_window(pdesc: AppendDesc, idesc: IndexDesc, adesc: AttnDesc, k_ne
         _ptr(q), _ptr(gate), _ptr(ids), _ptr(n_sel), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
         "qsa_decode_window")
+
+
+def qsa_step_workspace(idesc: IndexDesc, adesc: AttnDesc) -> int:
+    return int(lib().qsa_step_workspace(ctypes.byref(idesc), ctypes.byref(adesc)))
+
+
+def qsa_step(pdesc: AppendDesc, idesc: IndexDesc, adesc: AttnDesc, k_new, v_new, kidx_new, Kq,
+             Ksc, Vq, Vsc, K_idx, q_idx, q, gate, ids, n_sel, out, ws, stream=None) -> None:
+    _check(lib().qsa_step(
+        ctypes.byref(pdesc), ctypes.byref(idesc), ctypes.byref(adesc), _ptr(k_new), _ptr(v_new),
+        _ptr(kidx_new), _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc), _ptr(K_idx), _ptr(q_idx),
+        _ptr(q), _ptr(gate), _ptr(ids), _ptr(n_sel), _ptr(out), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "qsa_step")
+
+
+class StepCall:
+    """One prepared qsa_step call: the descriptors and raw device pointers
+    are marshalled once, so each call() is a single C call with no per-call
+    Python work beyond it (for timing loops)."""
+
+    def __init__(self, pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
+                 q_idx, q, gate, ids, n_sel, out, ws, stream=None):
+        self._keep = (pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
+                      q_idx, q, gate, ids, n_sel, out, ws)
+        self._args = (ctypes.byref(pdesc), ctypes.byref(idesc), ctypes.byref(adesc),
+                      _ptr(k_new), _ptr(v_new), _ptr(kidx_new), _ptr(Kq), _ptr(Ksc), _ptr(Vq),
+                      _ptr(Vsc), _ptr(K_idx), _ptr(q_idx), _ptr(q), _ptr(gate), _ptr(ids),
+                      _ptr(n_sel), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                      _stream(stream))
+        self._fn = lib().qsa_step
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(rc, "qsa_step")
 
 
 # ------------------------------------------------------- whole-path plan ---
@@ -259,6 +308,11 @@ class QsaPath:
             qsa_merge(self.adesc, self.partials, self.out, stream)
         else:
             qsa_merge_gated(self.adesc, self.partials, gate, self.out, stream)
+
+    def attend_merge(self, q, Kq, Ksc, Vq, Vsc, stream=None, gate=None, ids=None,
+                     n_sel=None):
+        qsa_attend_merge(self.adesc, q, Kq, Ksc, Vq, Vsc, self.ids if ids is None else ids,
+                         self.n_sel if n_sel is None else n_sel, gate, self.out, stream)
 
     def run(self, dev: dict, stream=None):
         self.index(dev["q_idx"], dev["K_idx"], stream)
