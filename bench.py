@@ -13,9 +13,11 @@ The default workload is the decode step (1 token, 24 x 256 query heads,
 independent caches, so the working set (~2.7 GB) is far larger than the
 256 MB last-level cache and every step streams from HBM.
 
-Timing: the K timed steps run back to back between two HIP events on the
-launch stream (nothing else is enqueued between them); four more such
-blocks give the median/min/max over rounds.  A separate pass of the same
+Timing: after the W warm-up steps, untimed steps continue until about 0.1 s
+of GPU time has passed (this GPU's clocks settle under a sustained HBM load
+only after some tens of milliseconds).  The K timed steps then run back to
+back between two HIP events on the launch stream (nothing else is enqueued
+between them); four more such blocks give the median/min/max over rounds.  A separate pass of the same
 calls one by one, with an event between stages, gives the per-stage
 breakdown (each event adds a few microseconds of its own), and the
 roofline's kernel time is the average of ten back-to-back launches of the
@@ -91,7 +93,7 @@ def attend_flops(p: dict, n_sel_total: int) -> float:
 # Source file of each attend kernel family (its hash gates profiled traffic).
 ATTEND_SOURCES = {"matrix": "qsa_attend_mma.hip", "vector": "qsa_attend.hip"}
 ATTEND_KERNELS = {"matrix": "k_attend_mma", "vector": "k_attend",
-                  "matrix_merge": "k_attend_merge_mma"}
+                  "matrix_merge": "k_attend_merge_mma", "matrix_mch": "k_attend_mch_mma"}
 # Headers whose code the attend kernels compile in (also hashed).
 ATTEND_HEADERS = ("qsa_device.h", "qsa_mma.h", "qsa_attend_mma.h", "qsa_merge.h")
 # Source and headers of the index kernels (their hash gates profiled index
@@ -132,7 +134,7 @@ def profiled_index_traffic(workload: str, B: int, P: int, algo: str, layout: str
 
 
 def profiled_traffic(workload: str, B: int, P: int, algo: str, layout: str = "dense"):
-    src_algo = "matrix" if algo == "matrix_merge" else algo
+    src_algo = "matrix" if algo.startswith("matrix") else algo
     """HBM bytes per attend dispatch from the committed rocprofv3 summary of
     this exact launch configuration
     (profiles/<kernel>_<workload>_b<B>_P<P>[_<layout>].md), scaled by the
@@ -238,6 +240,27 @@ def hbm_ceiling(inp: dict, dev: dict, path, B: int, P: int, attend_bytes: int,
                    gather_us=round(t * 1e6, 1),
                    attend_gather_gbs=round(gathered / (attend_ms * 1e-3) / 1e9, 1))
     return res
+
+
+def warm_up_to_steady_clocks(step, stream, seconds: float = 0.1) -> None:
+    """Untimed steps, enqueued back to back with no synchronisation between
+    them, for about `seconds` of GPU time.  After a period of low load this
+    GPU runs a sustained HBM-bound load about 7% slower for the first 10-30
+    ms (measured: decode steps of ~250 us settling at ~236 us, and a warm-up
+    broken by a host synchronisation every few milliseconds did not settle
+    it), so the timed steps start only after one continuous run."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_step = max(e0.elapsed_time(e1) * 1e-3 / 10, 1e-6)
+    for _ in range(int(math.ceil(seconds / per_step))):
+        step()
+    torch.cuda.synchronize()
 
 
 def host_record() -> dict:
@@ -498,6 +521,7 @@ def main() -> None:
     for _ in range(W):
         step()
     torch.cuda.synchronize()
+    warm_up_to_steady_clocks(step, stream)
     n_sel_total = int(path.n_sel.sum().item())
     by = algorithmic_bytes(inp, B, n_sel_total)
     fused_att_bytes = by["attend"] + (by["out"] if fused else 0)
@@ -527,8 +551,7 @@ def main() -> None:
     if not args.no_ceiling:
         ceiling = hbm_ceiling(inp, dev, path, B, P, fused_att_bytes,
                               kernel_ms(attend_call))
-        for _ in range(W):
-            step()
+        warm_up_to_steady_clocks(step, stream)
 
     def timed_block():
         """K steps between two events on the launch stream (nothing else
@@ -580,7 +603,10 @@ def main() -> None:
     elif dom == 2:
         # Matrix kernel: the products run on the matrix cores far below
         # their peak; the gathers of the kept cells bound it.
-        kalgo = "matrix_merge" if fused else "matrix"
+        # (P a multiple of 4 above 4 with >= 512 (token, KV head) pairs:
+        # the several-chunks-per-wave kernel)
+        mch = P % 4 == 0 and P > 4 and B * inp["T"] * inp["Hkv"] >= 512
+        kalgo = "matrix_merge" if fused else ("matrix_mch" if mch else "matrix")
         achieved = att_bytes / (att_ms * 1e-3) / 1e9
         roof = dict(kernel=ATTEND_KERNELS[kalgo], bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),

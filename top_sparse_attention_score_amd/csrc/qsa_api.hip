@@ -542,6 +542,12 @@ int qsa_step(const qsa_append_desc* pdesc, const qsa_index_desc* idesc,
     at.pm = part;
     at.pl = part + rows;
     at.po = part + 2 * rows;
+    if (qsa::attend_mch(at)) {
+        // several chunks per wave: the kernel merges the partials it wrote
+        if (qsa::launch_attend(at, s) != hipSuccess)
+            return QSA_ERR_HIP;
+        return QSA_OK;
+    }
     void* out_keep = at.out;
     at.out = nullptr;  // qsa_attend writes the partials
     if (qsa::launch_attend(at, s) != hipSuccess)

@@ -58,29 +58,47 @@ __device__ __forceinline__ uint16_t scale_bits(float a)
 }
 
 // Lane w of the quantisation items: 8 lanes per 32-element block of K or
-// V (4 elements each; the block maximum is combined over the 8 consecutive
-// lanes, so all 8 lanes of a group must call this together; `live` false
-// makes a lane take part in the shuffles only).
+// V, 4 elements each.
 // w = ((((b * T + t) * Hkv + g) * NB + sb32) * 2 + which) * 8 + sub
-__device__ __forceinline__ void append_quant_lane(const AppendLaunch& a, long long w, bool live)
+struct QuantLane {
+    int b, t, g, sb32, which, sub;
+};
+
+__device__ __forceinline__ QuantLane quant_lane(const AppendLaunch& a, long long w)
 {
     const int NB = a.D / 32;
-    const int sub = (int)(w & 7);
+    QuantLane q;
+    q.sub = (int)(w & 7);
     long long r = w >> 3;
-    const int which = (int)(r & 1);
+    q.which = (int)(r & 1);
     r >>= 1;
-    const int sb32 = (int)(r % NB);  // 32-element block of the row
+    q.sb32 = (int)(r % NB);  // 32-element block of the row
     r /= NB;
-    const int g = (int)(r % a.Hkv);
+    q.g = (int)(r % a.Hkv);
     r /= a.Hkv;
-    const int t = (int)(r % a.T);
-    const int b = (int)(r / a.T);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (live) {
-        const float* src = (which ? a.v_new : a.k_new) +
-                           (((size_t)b * a.T + t) * a.Hkv + g) * a.D + 32 * sb32 + 4 * sub;
-        v = *(const float4*)src;
-    }
+    q.t = (int)(r % a.T);
+    q.b = (int)(r / a.T);
+    return q;
+}
+
+// The lane's 4 new fp32 elements.
+__device__ __forceinline__ float4 append_quant_load(const AppendLaunch& a, long long w)
+{
+    const QuantLane q = quant_lane(a, w);
+    const float* src = (q.which ? a.v_new : a.k_new) +
+                       (((size_t)q.b * a.T + q.t) * a.Hkv + q.g) * a.D + 32 * q.sb32 + 4 * q.sub;
+    return *(const float4*)src;
+}
+
+// Quantise and store the lane's 4 elements v: the block maximum is combined
+// over the 8 consecutive lanes of the block, so all 8 lanes of a group must
+// call this together; `live` false makes a lane take part in the shuffles
+// only.
+__device__ __forceinline__ void append_quant_store(const AppendLaunch& a, long long w, float4 v,
+                                                   bool live)
+{
+    const int NB = a.D / 32;
+    const QuantLane q = quant_lane(a, w);
     float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1)
@@ -100,15 +118,30 @@ __device__ __forceinline__ void append_quant_lane(const AppendLaunch& a, long lo
         }
         word |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * e);
     }
-    const long long cell = (long long)(a.pos0 + t);
-    int8_t* codes = (which ? a.Vq : a.Kq) + (long long)b * (which ? a.vq_bs : a.kq_bs) +
-                    cell * (which ? a.vq_cs : a.kq_cs) + (long long)g * a.D + 32 * sb32 + 4 * sub;
+    const long long cell = (long long)(a.pos0 + q.t);
+    int8_t* codes = (q.which ? a.Vq : a.Kq) + (long long)q.b * (q.which ? a.vq_bs : a.kq_bs) +
+                    cell * (q.which ? a.vq_cs : a.kq_cs) + (long long)q.g * a.D + 32 * q.sb32 +
+                    4 * q.sub;
     *(uint32_t*)codes = word;
-    if (sub == 0) {
-        char* sc = (char*)(which ? a.Vsc : a.Ksc) + (long long)b * (which ? a.vsc_bs : a.ksc_bs) +
-                   cell * (which ? a.vsc_cs : a.ksc_cs) + ((long long)g * NB + sb32) * 2;
+    if (q.sub == 0) {
+        char* sc = (char*)(q.which ? a.Vsc : a.Ksc) +
+                   (long long)q.b * (q.which ? a.vsc_bs : a.ksc_bs) +
+                   cell * (q.which ? a.vsc_cs : a.ksc_cs) + ((long long)q.g * NB + q.sb32) * 2;
         *(uint16_t*)sc = sb;
     }
+}
+
+// Both steps for lane w (see above).
+__device__ __forceinline__ void append_quant_lane(const AppendLaunch& a, long long w, bool live)
+{
+    const float4 v = live ? append_quant_load(a, w) : make_float4(0.f, 0.f, 0.f, 0.f);
+    append_quant_store(a, w, v, live);
+}
+
+// fp16 bits of two floats (nearest, ties to even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_half2_rne(float lo, float hi)
+{
+    return (uint32_t)f16_bits((_Float16)lo) | ((uint32_t)f16_bits((_Float16)hi) << 16);
 }
 
 // Lane r of the index-key items: 4 elements of (b, t), r = (b * T + t) *
@@ -121,11 +154,8 @@ __device__ __forceinline__ void append_index_lane(const AppendLaunch& a, long lo
     const int t = (int)(bt % a.T);
     const int b = (int)(bt / a.T);
     const float4 v = ((const float4*)(a.kidx_new + (size_t)bt * a.DI))[i];
-    const uint16_t h0 = f16_bits((_Float16)v.x), h1 = f16_bits((_Float16)v.y);
-    const uint16_t h2 = f16_bits((_Float16)v.z), h3 = f16_bits((_Float16)v.w);
     uint16_t* dst = a.K_idx + ((size_t)b * a.N + a.pos0 + t) * a.DI + 4 * i;
-    ((uint2*)dst)[0] = make_uint2((uint32_t)h0 | ((uint32_t)h1 << 16),
-                                  (uint32_t)h2 | ((uint32_t)h3 << 16));
+    ((uint2*)dst)[0] = make_uint2(pack_half2_rne(v.x, v.y), pack_half2_rne(v.z, v.w));
 }
 
 // Items: the quantisation lanes, then one lane per 4 index-key elements.

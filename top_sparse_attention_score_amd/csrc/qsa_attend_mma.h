@@ -18,8 +18,10 @@
 //     so hi + lo carries 22 significant bits, and each product is issued
 //     twice (hi, then lo) into the same fp32 accumulator;
 //   - a softmax weight times a V scale is split the same way (hi rounded
-//     toward zero, so x - hi is exact), the weight carried at 2^4 times its
-//     value so the lo half stays clear of the fp16 subnormal range.
+//     toward zero; lo is the exact product minus hi, formed in one mixed
+//     fp32/fp16 FMA and rounded toward zero), the weight carried at 2^4
+//     times its value so the lo half stays clear of the fp16 subnormal
+//     range.
 // Two exact power-of-two shifts keep every half finite and normal whatever
 // the magnitudes: an item's fp32 query is split as q * 2^-eq with its
 // largest |q| in [2^14, 2^15) (the logits are scaled back by 2^eq), and a
@@ -86,7 +88,17 @@ constexpr int kMmaWaves = 4;      // (token, chunk) items per workgroup
 // output equals qsa_attend followed by qsa_merge(_gated) bit for bit.
 // Every wave, also one with an empty chunk or past the last item, takes
 // part in the workgroup barriers of that epilogue.
-template <int G, int D, bool QF16, bool SHQ, bool MERGE = false>
+//
+// MCH (with SHQ, without MERGE): one workgroup per (token, KV head) of a
+// split with P a multiple of 4; wave w computes chunks w, w + 4, ..., one
+// after another, writing each chunk's partial when it ends, and gathers the
+// next chunk's first tile while the current chunk's last tile runs, so a
+// wave's gathers never drain between chunks.  Each partial is computed with
+// the same operations as in the one-chunk-per-wave mapping (bit-equal).
+// With `out` set, the workgroup then merges its token's partials (read back
+// from memory it wrote itself, after a workgroup barrier) with the merge
+// kernel's sequence and writes the gated output.
+template <int G, int D, bool QF16, bool SHQ, bool MERGE = false, bool MCH = false>
 __device__ __forceinline__ void attend_mma_block(
     int wg, const void* __restrict__ q, const int8_t* __restrict__ Kq,
     const uint8_t* __restrict__ Ksc, const int8_t* __restrict__ Vq,
@@ -98,6 +110,7 @@ __device__ __forceinline__ void attend_mma_block(
     int out_f16 = 0)
 {
     static_assert(G <= 16, "one 16-row head block per KV head");
+    static_assert(!MCH || (SHQ && !MERGE), "several chunks per wave: shared query, partials");
     constexpr int NB = D / 32;                // scale blocks per head row
     constexpr int NT = D / 16;                // 16-element slices (= 16-byte chunks)
     constexpr int NPR = NB / 2;               // 32-bit scale words per head row
@@ -125,12 +138,13 @@ __device__ __forceinline__ void attend_mma_block(
     // lines both heads touch (scales, ids).  The grid is padded to a
     // multiple of 8 Hkv.
     const int g = (wg >> 3) % Hkv;
+    // (With MCH a group is one token.)
     const long long group = (long long)(wg / (8 * Hkv)) * 8 + (wg & 7);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long long item = group * kMmaWaves + wave;
+    const long long item = MCH ? group * P + wave : group * kMmaWaves + wave;
     const int lane = threadIdx.x & 63;
     const int hq = lane & 15, q4 = lane >> 4;
-    if (group * kMmaWaves >= (long long)BT * P)
+    if ((MCH ? group * P : group * kMmaWaves) >= (long long)BT * P)
         return;  // grid padding (whole workgroup)
 
     if constexpr (MERGE) {
@@ -159,7 +173,7 @@ __device__ __forceinline__ void attend_mma_block(
     if constexpr (SHQ) {
         // Every wave of the block has the same token (P % 4 == 0 and the grid
         // covers whole blocks of items); each builds some query blocks.
-        const int bt0 = (int)((group * kMmaWaves) / P);
+        const int bt0 = (int)(MCH ? group : (group * kMmaWaves) / P);
         const size_t prow0 = (size_t)bt0 * Hq + (size_t)g * G;
         if constexpr (!QF16) {
             float amax = 0.f;
@@ -186,7 +200,8 @@ __device__ __forceinline__ void attend_mma_block(
         if (!live)
             return;
     }
-    const int bt = live ? (int)(item / P) : 0, c = live ? (int)(item % P) : 0;
+    const int bt = live ? (int)(item / P) : 0;
+    int c = live ? (int)(item % P) : 0;
     int8_t* v_s = v_all[wave];
     uint32_t* vsc_s = vsc_all[wave];
     float* p_s = p_all[wave];
@@ -195,18 +210,22 @@ __device__ __forceinline__ void attend_mma_block(
 
     const int ns = live ? min(n_sel[bt], cap) : 0;
     const int S = (ns + P - 1) / P;
-    const int beg = c * S;
-    const int end = min(beg + S, ns);
+    int beg = c * S;
+    int end = min(beg + S, ns);
 
-    if (!MERGE && beg >= end) {
+    // Partial of an empty chunk cc: (-inf, 0, 0).
+    auto write_empty = [&](int cc) {
         if (lane < G) {
-            pm[(prow + lane) * P + c] = -INFINITY;
-            pl[(prow + lane) * P + c] = 0.f;
+            pm[(prow + lane) * P + cc] = -INFINITY;
+            pl[(prow + lane) * P + cc] = 0.f;
         }
         for (int i = lane; i < G * D / 4; i += 64) {
             const int h = i / (D / 4), e = i % (D / 4);
-            *(float4*)(po + ((prow + h) * P + c) * D + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
+            *(float4*)(po + ((prow + h) * P + cc) * D + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    };
+    if (!MERGE && !MCH && beg >= end) {
+        write_empty(c);
         return;
     }
 
@@ -223,7 +242,33 @@ __device__ __forceinline__ void attend_mma_block(
         o[t] = float4_t{0.f, 0.f, 0.f, 0.f};
     int ev = 0;  // the accumulated output carries 2^ev (see the header)
 
-    if (beg < end) {  // always true here without MERGE
+    // Partial of chunk cc: m, and l, o brought from the reference max to m.
+    auto write_partial = [&](int cc) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * q4 + r;
+            const float f = __builtin_amdgcn_exp2f((m_ref[r] - m_run[r]) * kLog2e);
+            if (hq == 0) {
+                p_s[h * PP + 33] = f;
+                if (h < G) {
+                    pm[(prow + h) * P + cc] = m_run[r];
+                    pl[(prow + h) * P + cc] = l_run[r] * f;
+                }
+            }
+        }
+        wave_lds_sync();
+        if (hq < G) {
+            const float f = __builtin_amdgcn_ldexpf(p_s[hq * PP + 33] * (1.f / kWScale), -ev);
+            float* dst = po + ((prow + hq) * P + cc) * D + 4 * q4;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float4_t v = o[t] * f;
+                *(float4*)(dst + 16 * t) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    };
+
+    if (beg < end) {  // always true here without MERGE or MCH
     half8_t qh[SHQ ? 1 : NB], ql[SHQ ? 1 : NB];
     if constexpr (!SHQ) {
         if constexpr (!QF16) {
@@ -294,9 +339,19 @@ __device__ __forceinline__ void attend_mma_block(
 
 #pragma unroll 1
     for (;;) {
-        const int t1 = t0 + TC;
-        const bool more = t1 < end;
-        const int nt1 = more ? min(TC, end - t1) : 0;
+        // Next tile: the next one of this chunk or (MCH) the first one of the
+        // wave's next chunk, if that chunk has cells.
+        int t1 = t0 + TC, end1 = end;
+        bool more = t1 < end;
+        if constexpr (MCH) {
+            const int cn = c + kMmaWaves;
+            if (!more && cn < P && cn * S < ns) {
+                more = true;
+                t1 = cn * S;
+                end1 = min(t1 + S, ns);
+            }
+        }
+        const int nt1 = more ? min(TC, end1 - t1) : 0;
         int jvn = 0, jan = 0, jbn = 0;
         // The K registers were loaded during the previous PV phase; settle
         // them first so the V copy below overlaps the whole QK phase.
@@ -433,12 +488,11 @@ __device__ __forceinline__ void attend_mma_block(
                         (lds_int2v_t*)(v_rd + 512 * (4 * pr + u)));
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        x[e] = hb ? mul_by_half<1>(pw[e], sw[e]) : mul_by_half<0>(pw[e], sw[e]);
                     half8_t whi, wlo;
-                    split8(x, whi, wlo);
+                    if (hb)
+                        split8_prod<1>(pw, sw, whi, wlo);
+                    else
+                        split8_prod<0>(pw, sw, whi, wlo);
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const int t = 4 * pr + 2 * hb + u;  // slice of scale block 2*pr + hb
@@ -451,6 +505,26 @@ __device__ __forceinline__ void attend_mma_block(
             }
         }
         wave_lds_sync();  // LDS reads done before the next tile's copies
+        if constexpr (MCH) {
+            if (t0 + TC >= end) {  // the chunk is done: its partial, then a fresh state
+                write_partial(c);
+                if (more) {
+                    c += kMmaWaves;
+                    beg = t1;
+                    end = end1;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        m_run[r] = -INFINITY;
+                        m_ref[r] = -INFINITY;
+                        l_run[r] = 0.f;
+                    }
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        o[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+                    ev = 0;
+                }
+            }
+        }
         if (!more)
             break;
         t0 = t1;
@@ -460,30 +534,29 @@ __device__ __forceinline__ void attend_mma_block(
 
     }  // beg < end
 
-    if constexpr (!MERGE) {
-        // ---- partials: m, and l, o brought from the reference max to m -----
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = 4 * q4 + r;
-            const float f = __builtin_amdgcn_exp2f((m_ref[r] - m_run[r]) * kLog2e);
-            if (hq == 0) {
-                p_s[h * PP + 33] = f;
-                if (h < G) {
-                    pm[(prow + h) * P + c] = m_run[r];
-                    pl[(prow + h) * P + c] = l_run[r] * f;
-                }
+    if constexpr (MCH) {
+        // The wave's chunks after its last one with cells are empty (chunks
+        // with cells form a prefix), as are all of them if the first is.
+        for (int cc = (beg < end) ? c + kMmaWaves : c; cc < P; cc += kMmaWaves)
+            write_empty(cc);
+        if (out) {
+            // Merge the token's P partials of this KV head's G query heads.
+            __syncthreads();  // the partial stores of every wave are visible
+            for (int i = threadIdx.x; i < G * (D / 4); i += 64 * kMmaWaves) {
+                const int h = i / (D / 4), d4 = i % (D / 4);
+                const size_t row = prow + h;
+                float res[4];
+                merge_elems<4>(pm + row * P, pl + row * P, 1, po + row * P * D + 4 * d4, D, P,
+                               res);
+                const long long off = (long long)row * D + 4 * d4;
+                if (out_f16)
+                    gate_store<4, true>(res, gate, QF16 ? 1 : 0, off, out, off);
+                else
+                    gate_store<4, false>(res, gate, QF16 ? 1 : 0, off, out, off);
             }
         }
-        wave_lds_sync();
-        if (hq < G) {
-            const float f = __builtin_amdgcn_ldexpf(p_s[hq * PP + 33] * (1.f / kWScale), -ev);
-            float* dst = po + ((prow + hq) * P + c) * D + 4 * q4;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const float4_t v = o[t] * f;
-                *(float4*)(dst + 16 * t) = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        }
+    } else if constexpr (!MERGE) {
+        write_partial(c);
     } else {
         // ---- fused merge: the same partial values, merged in LDS ------------
         // m and l of head h at slots 34 and 35 of row h of the wave's weight

@@ -811,10 +811,14 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_row(const uint32_t* __restr
 // threads score the visible key rows (16 lanes per 256-byte row as in
 // k_idx_scan, eight rows in flight per lane) into an LDS key table, then
 // select from it.  Used while the row's keys fit in LDS.
-// APPEND: the workgroup first writes its problem's new token into the cache
-// (the lanes qsa_kv_append runs for that problem), so the scan below reads
-// the new cell's index key; the barrier orders the writes before the reads
-// (one workgroup, one CU).
+// APPEND: the workgroup also writes its problem's new token (T == 1) into
+// the cache, off the scan's critical path: the new rows are loaded at the
+// start; the scan skips the new cell's key row (its old contents); after
+// the scan one row group scores the new fp16 key with the scan's own
+// arithmetic (same dot2 sequence and row reduction, so the same fp32 score
+// the scan would compute from the written key) and writes the key, and the
+// quantisation lanes of qsa_kv_append for this problem write the codes and
+// scales.  Needs Hkv * D / 2 <= kRowThreads quantisation lanes.
 template <int DI, int KPT, bool APPEND>
 __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __restrict__ q_idx,
                                                              const uint4* __restrict__ K_idx,
@@ -823,10 +827,6 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
                                                              int pos0, int k, int dense_max, int cap,
                                                              AppendLaunch ap)
 {
-    if constexpr (APPEND) {
-        append_problem(ap, blockIdx.x, kRowThreads);
-        __syncthreads();
-    }
     constexpr int LPR = DI / 8;                // lanes per key row
     constexpr int RPS = kRowThreads / LPR;     // rows per block-wide step
     constexpr int U = 16;                      // steps in flight per thread
@@ -838,11 +838,33 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
     const int nvis = pos0 + 1;
     int32_t* out = ids + (size_t)b * cap;
     if (!token_selects(nvis, k, dense_max)) {
+        if constexpr (APPEND) {
+            append_problem(ap, b, kRowThreads);
+        }
         dense_row(nvis, cap, out, n_sel + b);
         return;
     }
     const int tid = threadIdx.x;
     const int sub = tid % LPR;
+    // APPEND: this lane's new K/V elements and (wave 0) its part of the new
+    // index key, loaded now and used after the scan.
+    const long long nq = APPEND ? (long long)ap.Hkv * (ap.D / 32) * 16 : 0;
+    const bool qlane = tid < nq;
+    const long long wq = (long long)b * nq + tid;
+    const bool newkey = APPEND && ap.kidx_new != nullptr;
+    float4 nv = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint4 nkey = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (APPEND) {
+        if (qlane)
+            nv = append_quant_load(ap, wq);
+        if (newkey && tid < 64) {
+            const float4* src = (const float4*)(ap.kidx_new + (size_t)b * DI) + 2 * sub;
+            const float4 x0 = src[0], x1 = src[1];
+            nkey = make_uint4(pack_half2_rne(x0.x, x0.y), pack_half2_rne(x0.z, x0.w),
+                              pack_half2_rne(x1.x, x1.y), pack_half2_rne(x1.z, x1.w));
+        }
+    }
+    const int jnew = newkey ? nvis - 1 : -1;  // the new cell: scored after the scan
     const uint4 qv = q_idx[(size_t)b * (DI / 8) + sub];
     const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
     const uint4* Kb = K_idx + (size_t)b * N * (DI / 8) + sub;
@@ -862,9 +884,26 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
             for (int e = 0; e < 4; ++e)
                 acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
             acc = row_sum<LPR>(acc);
-            if (sub == 0 && j < nvis)
+            if (sub == 0 && j < nvis && j != jnew)
                 keys_s[j] = score_key(acc);
         }
+    }
+    if constexpr (APPEND) {
+        if (newkey && tid < 64) {
+            // wave 0: the new cell's score as the loop computes it
+            const uint32_t kw[4] = {nkey.x, nkey.y, nkey.z, nkey.w};
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
+            acc = row_sum<LPR>(acc);
+            if (tid == 0)
+                keys_s[jnew] = score_key(acc);
+            if (tid < LPR)
+                *((uint4*)(ap.K_idx + ((size_t)b * ap.N + ap.pos0) * DI) + sub) = nkey;
+        }
+        if (qlane)
+            append_quant_store(ap, wq, nv, true);  // whole 8-lane groups (nq % 16 == 0)
     }
     __syncthreads();
     const int c0 = tid * KPT;
@@ -1595,9 +1634,17 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLa
         const uint4* q = (const uint4*)a.q_idx;
         const uint4* K = (const uint4*)a.K_idx;
         const AppendLaunch none{};
+        // The scan kernel's workgroups write the new tokens while they fit
+        // its quantisation lanes; otherwise the append kernel runs first.
+        const bool fold = ap && (long long)ap->Hkv * ap->D / 2 <= kRowThreads;
+        if (ap && !fold) {
+            const hipError_t e = launch_kv_append(*ap, s);
+            if (e != hipSuccess)
+                return e;
+        }
 #define QSA_FUSED(DI, KPT)                                                                      \
     do {                                                                                        \
-        if (ap)                                                                                 \
+        if (fold)                                                                               \
             k_scan_select<DI, KPT, true><<<a.B, kRowThreads, 0, s>>>(                           \
                 q, K, a.ids, a.n_sel, a.N, a.pos0, a.k, a.dense_max, a.cap, *ap);               \
         else                                                                                    \

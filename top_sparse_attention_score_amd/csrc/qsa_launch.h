@@ -77,7 +77,11 @@ hipError_t launch_attend(const AttnLaunch& a, hipStream_t s);
 // Matrix-core attend kernel (qsa_attend_mma.hip); false if no variant fits.
 // With a.out set (P in {1, 2, 4}) the kernel also merges the chunks, applies
 // a.gate and writes a.out instead of the partials.
+// With a.P a multiple of 4 above 4 and at least 512 (token, KV head) pairs,
+// the kernel runs several chunks per wave (attend_mch); then a.out, if set,
+// also makes it merge the partials it wrote (a.pm/pl/po must be set).
 bool launch_attend_mma(const AttnLaunch& a, hipStream_t s);
+bool attend_mch(const AttnLaunch& a);
 hipError_t launch_merge(const AttnLaunch& a, hipStream_t s);
 
 // Single-launch decode window (qsa_window.hip): append, index, attend and

@@ -56,14 +56,43 @@ __device__ __forceinline__ float mul_by_half(float a, uint32_t w)
     return r;
 }
 
-// Splits eight fp32 values into fp16 hi (round toward zero) and lo = x - hi
-// (exact in fp32, then rounded toward zero to fp16).
-__device__ __forceinline__ void split8(const float* x, half8_t& hi, half8_t& lo)
+// a * (fp16 half HI of w) - (fp16 half LO of h) in one mixed-precision FMA:
+// both fp16 operands are widened exactly, the result is rounded once.
+template <int HI, int LO>
+__device__ __forceinline__ float fma_half_minus_half(float a, uint32_t w, uint32_t h)
+{
+    float r;
+    if constexpr (HI && LO)
+        asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+            : "=v"(r) : "v"(a), "v"(w), "v"(h));
+    else if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,1,0] op_sel_hi:[0,1,1]"
+            : "=v"(r) : "v"(a), "v"(w), "v"(h));
+    else if constexpr (LO)
+        asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
+            : "=v"(r) : "v"(a), "v"(w), "v"(h));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]"
+            : "=v"(r) : "v"(a), "v"(w), "v"(h));
+    return r;
+}
+
+// The eight products x_e = a_e * s_e (s_e the fp16 half HI of w_e) as fp16
+// hi + lo: hi = fp16(fp32(x_e)) rounded toward zero, lo = fp16(x_e - hi)
+// rounded toward zero, with x_e - hi formed from the exact product in one
+// mixed FMA.  hi + lo carries x_e to 22 significant bits.
+template <int HI>
+__device__ __forceinline__ void split8_prod(const float* a, const uint32_t* w, half8_t& hi,
+                                            half8_t& lo)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const auto h = __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]);
-        const auto l = __builtin_amdgcn_cvt_pkrtz(x[2 * i] - (float)h[0], x[2 * i + 1] - (float)h[1]);
+        const auto h = __builtin_amdgcn_cvt_pkrtz(mul_by_half<HI>(a[2 * i], w[2 * i]),
+                                                  mul_by_half<HI>(a[2 * i + 1], w[2 * i + 1]));
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const auto l = __builtin_amdgcn_cvt_pkrtz(fma_half_minus_half<HI, 0>(a[2 * i], w[2 * i], hb),
+                                                  fma_half_minus_half<HI, 1>(a[2 * i + 1],
+                                                                            w[2 * i + 1], hb));
         hi[2 * i] = (_Float16)h[0];
         hi[2 * i + 1] = (_Float16)h[1];
         lo[2 * i] = (_Float16)l[0];
