@@ -153,23 +153,26 @@ def profiled_traffic(workload: str, B: int, P: int, algo: str, layout: str = "de
 
 def interleave_cache(dev: dict, B: int, N: int, Hkv: int, D: int):
     """The cache as one row per cell: every head's K codes, then V codes,
-    then K scales, then V scales (Hkv*(2D + D/8) bytes); returns device views
+    then K scales, then V scales (Hkv*(2D + D/8) bytes, each scale region
+    padded to 16 bytes); returns device views
     at the four bases and the attention/append strides (bytes) that address
     them.  The four regions of a cell are disjoint, so the append writes and
     the attention reads the same cells as with the dense arrays."""
     import torch
     codes, sc = Hkv * D, Hkv * (D // 32) * 2
-    row = 2 * codes + 2 * sc
-    buf = torch.empty((B, N, row), dtype=torch.int8, device="cuda")
+    scp = (sc + 15) // 16 * 16         # each scale region 16-byte aligned
+    row = 2 * codes + 2 * scp          # (1088 B for 2 heads of 256: no padding)
+    buf = torch.zeros((B, N, row), dtype=torch.int8, device="cuda")
     buf[:, :, :codes].copy_(dev["Kq"].reshape(B, N, codes))
     buf[:, :, codes:2 * codes].copy_(dev["Vq"].reshape(B, N, codes))
-    buf[:, :, 2 * codes:2 * codes + sc].copy_(dev["Ksc"].reshape(B, N, -1).view(torch.int8))
-    buf[:, :, 2 * codes + sc:].copy_(dev["Vsc"].reshape(B, N, -1).view(torch.int8))
+    ks, vs = 2 * codes, 2 * codes + scp
+    buf[:, :, ks:ks + sc].copy_(dev["Ksc"].reshape(B, N, -1).view(torch.int8))
+    buf[:, :, vs:vs + sc].copy_(dev["Vsc"].reshape(B, N, -1).view(torch.int8))
     out = dict(dev)
     out["Kq"] = buf[:, :, :codes]
     out["Vq"] = buf[:, :, codes:2 * codes]
-    out["Ksc"] = buf[:, :, 2 * codes:2 * codes + sc]
-    out["Vsc"] = buf[:, :, 2 * codes + sc:]
+    out["Ksc"] = buf[:, :, ks:ks + sc]
+    out["Vsc"] = buf[:, :, vs:vs + sc]
     out["kv_buffer"] = buf
     strides = {f"{n}_cell_stride": row for n in ("kq", "ksc", "vq", "vsc")}
     strides.update({f"{n}_batch_stride": row * N for n in ("kq", "ksc", "vq", "vsc")})
@@ -334,10 +337,10 @@ def cpu_baseline(inp_cfg: str, target_s: float, P: int) -> dict:
 
 def single_problem_latency(qsa, base: dict, P: int, algo_code: int, steps: int = 50) -> dict:
     """One problem (B = 1) per step, the latency-bound case: the same step
-    (append -> index_topk -> attend -> gated merge) launched eagerly, and
-    captured once in a HIP graph and replayed; then the step as the single
-    cooperative launch of qsa_decode_window (eagerly and from a graph);
-    microseconds per step."""
+    (qsa_step: append -> index_topk -> attend -> gated merge) launched
+    eagerly, and captured once in a HIP graph and replayed; then the step as
+    the single cooperative launch of qsa_decode_window (eagerly and from a
+    graph); microseconds per step."""
     import torch
     inp = {k: (v[:1] if hasattr(v, "shape") and getattr(v, "ndim", 0) and k in
                ("q_idx", "K_idx", "q", "Kq", "Ksc", "Vq", "Vsc") else v)
@@ -355,11 +358,13 @@ def single_problem_latency(qsa, base: dict, P: int, algo_code: int, steps: int =
                             d_idx=di)
     path = qsa.path_for(inp, P=P, algo=algo_code)
     side = torch.cuda.Stream()
+    ws_step = torch.empty(qsa.qsa_step_workspace(path.idesc, path.adesc) // 4 + 64,
+                          dtype=torch.int32, device="cuda")
 
     def step(stream=None):
-        qsa.qsa_kv_append(adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"], dev["Vq"],
-                          dev["Vsc"], dev["K_idx"], stream=stream)
-        path.run(dev, stream=stream)
+        qsa.qsa_step(adesc, path.idesc, path.adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"],
+                     dev["Vq"], dev["Vsc"], dev["K_idx"], dev["q_idx"], dev["q"], dev["gate"],
+                     path.ids, path.n_sel, path.out, ws_step, stream=stream)
 
     def timed(fn):
         for _ in range(5):
@@ -591,6 +596,12 @@ def main() -> None:
         names[2] = "attend_merge_gated"
     dom = int(np.argmax(stage_ms))
     att_bytes = fused_att_bytes
+    # The attention kernel of this shape (its committed profile also holds
+    # the index kernels' traffic): P a multiple of 4 above 4 with >= 512
+    # (token, KV head) pairs runs several chunks per wave.
+    mch = P % 4 == 0 and P > 4 and B * inp["T"] * inp["Hkv"] >= 512
+    kalgo = ("matrix_merge" if fused else ("matrix_mch" if mch else "matrix")) \
+        if args.algo == "matrix" else args.algo
     att_ms = stage_ms[2]
     if names[dom] == "attend" and args.algo == "vector":
         achieved = flops / (att_ms * 1e-3) / 1e12
@@ -603,10 +614,6 @@ def main() -> None:
     elif dom == 2:
         # Matrix kernel: the products run on the matrix cores far below
         # their peak; the gathers of the kept cells bound it.
-        # (P a multiple of 4 above 4 with >= 512 (token, KV head) pairs:
-        # the several-chunks-per-wave kernel)
-        mch = P % 4 == 0 and P > 4 and B * inp["T"] * inp["Hkv"] >= 512
-        kalgo = "matrix_merge" if fused else ("matrix_mch" if mch else "matrix")
         achieved = att_bytes / (att_ms * 1e-3) / 1e9
         roof = dict(kernel=ATTEND_KERNELS[kalgo], bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
@@ -617,7 +624,7 @@ def main() -> None:
         sb = {"index_topk": by["index"], "merge_gated": by["out"],
               "kv_append": by["append"]}[names[dom]]
         achieved = sb / (stage_ms[dom] * 1e-3) / 1e9
-        traffic = (profiled_index_traffic(args.workload, B, P, args.algo, args.layout)
+        traffic = (profiled_index_traffic(args.workload, B, P, kalgo, args.layout)
                    if names[dom] == "index_topk" else None)
         roof = dict(kernel=names[dom], bound="hbm", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),

@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_filter(SelWs w, int T, int 
 {
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t s_wave[kSelThreads / 64];
-    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_pick[3];
 
     const int bt = blockIdx.y;
     const int nvis = pos0 + (bt % T) + 1;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_pivot(SelWs w, int32_t* __r
 {
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t s_wave[kSelThreads / 64];
-    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_pick[3];
     __shared__ uint32_t c_key[kCap];
     __shared__ uint32_t c_idx[kCap];
     __shared__ uint32_t s_tile[kMaxTiles];
@@ -658,7 +658,14 @@ __device__ __forceinline__ uint32_t row_excl_scan(uint32_t v, uint32_t& total,
 // keys equal to it that rank within the k largest.  Radix digits of 11, 11
 // and 10 bits with LDS histograms.
 // `each(f)` calls f(key) for every key this thread holds.
-template <class Each>
+// PRE0: hist already holds the first digit's counts of the real keys (built
+// while the keys were produced; absent keys, all in bin 0 below every real
+// key there, do not change which bin holds the k-th key or its rank in it).
+// When the bin holding the k-th key must be kept whole (its count equals
+// the keys still needed), the selection is every key at or above the bin's
+// lowest key: the result is then (bin prefix) - 1 with r = 0, which keeps
+// exactly those keys, and the remaining digits are skipped.
+template <bool PRE0 = false, class Each>
 __device__ __forceinline__ uint32_t row_kth_largest_each(Each each, uint32_t k, uint32_t& r,
                                                          uint32_t* hist, uint32_t* s_wave,
                                                          uint32_t* s_pick)
@@ -670,14 +677,16 @@ __device__ __forceinline__ uint32_t row_kth_largest_each(Each each, uint32_t k, 
     for (int d = 0; d < 3; ++d) {
         const int shift = (d == 0) ? 21 : (d == 1) ? 10 : 0;
         const int nb = (d == 2) ? 1024 : 2048;
-        for (int i = tid; i < nb; i += kRowThreads)
-            hist[i] = 0u;
-        __syncthreads();
-        each([&](uint32_t v) {
-            if ((v & pmask) == prefix)
-                atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
-        });
-        __syncthreads();
+        if (!(PRE0 && d == 0)) {
+            for (int i = tid; i < nb; i += kRowThreads)
+                hist[i] = 0u;
+            __syncthreads();
+            each([&](uint32_t v) {
+                if ((v & pmask) == prefix)
+                    atomicAdd(&hist[(v >> shift) & (uint32_t)(nb - 1)], 1u);
+            });
+            __syncthreads();
+        }
         // Bin holding the r-th largest: thread t sums bins nb-1-2t and
         // nb-2-2t (nb / kRowThreads = 2 or 1 bins per thread).
         const int per = nb / kRowThreads;
@@ -695,6 +704,7 @@ __device__ __forceinline__ uint32_t row_kth_largest_each(Each each, uint32_t k, 
                 if (acc < r && r <= acc + cnt) {
                     s_pick[0] = (uint32_t)(hi - i);
                     s_pick[1] = acc;
+                    s_pick[2] = cnt;
                 }
                 acc += cnt;
             }
@@ -703,17 +713,22 @@ __device__ __forceinline__ uint32_t row_kth_largest_each(Each each, uint32_t k, 
         r -= s_pick[1];
         prefix |= s_pick[0] << shift;
         pmask |= (uint32_t)(nb - 1) << shift;
+        const bool whole = s_pick[2] == r && prefix != 0u && d < 2;
         __syncthreads();
+        if (whole) {
+            r = 0;
+            return prefix - 1u;
+        }
     }
     return prefix;
 }
 
-template <int KPT>
+template <int KPT, bool PRE0 = false>
 __device__ __forceinline__ uint32_t row_kth_largest(const uint32_t (&key)[KPT], uint32_t k,
                                                     uint32_t& r, uint32_t* hist, uint32_t* s_wave,
                                                     uint32_t* s_pick)
 {
-    return row_kth_largest_each(
+    return row_kth_largest_each<PRE0>(
         [&](auto f) {
 #pragma unroll
             for (int j = 0; j < KPT; ++j)
@@ -725,14 +740,15 @@ __device__ __forceinline__ uint32_t row_kth_largest(const uint32_t (&key)[KPT], 
 // Selects the k largest of the row's keys, which thread t holds for cells
 // c0 = t*KPT .. c0+KPT-1 (0 for cells past the token's position), and writes
 // the kept cells in ascending order, -1 padding and the count.
-template <int KPT>
+template <int KPT, bool PRE0 = false>
 __device__ __forceinline__ void select_row(const uint32_t (&key)[KPT], int c0, int k, int cap,
                                            int32_t* __restrict__ out, int32_t* __restrict__ n_out,
                                            uint32_t* hist, uint32_t* s_wave, uint32_t* s_pick)
 {
     const int tid = threadIdx.x;
     uint32_t r;
-    const uint32_t prefix = row_kth_largest<KPT>(key, (uint32_t)k, r, hist, s_wave, s_pick);
+    const uint32_t prefix =
+        row_kth_largest<KPT, PRE0>(key, (uint32_t)k, r, hist, s_wave, s_pick);
 
     // prefix is the k-th largest key; r keys equal to it are kept, lowest
     // cells first.
@@ -779,7 +795,7 @@ __global__ __launch_bounds__(kRowThreads) void k_sel_row(const uint32_t* __restr
 {
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t s_wave[kRowThreads / 64];
-    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_pick[3];
     const int row = blockIdx.x;
     const int nvis = pos0 + (row % T) + 1;
     int32_t* out = ids + (size_t)row * cap;
@@ -833,7 +849,7 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
     __shared__ uint32_t keys_s[kRowThreads * KPT];
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t s_wave[kRowThreads / 64];
-    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_pick[3];
     const int b = blockIdx.x;
     const int nvis = pos0 + 1;
     int32_t* out = ids + (size_t)b * cap;
@@ -865,6 +881,10 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
         }
     }
     const int jnew = newkey ? nvis - 1 : -1;  // the new cell: scored after the scan
+    // The select's first-digit histogram is counted as the keys are made.
+    for (int i = tid; i < 2048; i += kRowThreads)
+        hist[i] = 0u;
+    __syncthreads();
     const uint4 qv = q_idx[(size_t)b * (DI / 8) + sub];
     const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
     const uint4* Kb = K_idx + (size_t)b * N * (DI / 8) + sub;
@@ -884,8 +904,11 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
             for (int e = 0; e < 4; ++e)
                 acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
             acc = row_sum<LPR>(acc);
-            if (sub == 0 && j < nvis && j != jnew)
-                keys_s[j] = score_key(acc);
+            if (sub == 0 && j < nvis && j != jnew) {
+                const uint32_t kk = score_key(acc);
+                keys_s[j] = kk;
+                atomicAdd(&hist[kk >> 21], 1u);
+            }
         }
     }
     if constexpr (APPEND) {
@@ -897,8 +920,11 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
             for (int e = 0; e < 4; ++e)
                 acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
             acc = row_sum<LPR>(acc);
-            if (tid == 0)
-                keys_s[jnew] = score_key(acc);
+            if (tid == 0) {
+                const uint32_t kk = score_key(acc);
+                keys_s[jnew] = kk;
+                atomicAdd(&hist[kk >> 21], 1u);
+            }
             if (tid < LPR)
                 *((uint4*)(ap.K_idx + ((size_t)b * ap.N + ap.pos0) * DI) + sub) = nkey;
         }
@@ -911,7 +937,7 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
         key[j] = (c0 + j < nvis) ? keys_s[c0 + j] : 0u;
-    select_row<KPT>(key, c0, k, cap, out, n_sel + b, hist, s_wave, s_pick);
+    select_row<KPT, true>(key, c0, k, cap, out, n_sel + b, hist, s_wave, s_pick);
 }
 
 // ------------------------------------------ many tokens: fused select ---
@@ -1060,7 +1086,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_thresh(const uint32_t* __re
     constexpr int M = kSampleCells / kSelThreads;
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t s_wave[kSelThreads / 64];
-    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_pick[3];
     __shared__ uint32_t s_red[8];
     const int bt = blockIdx.x;
     const int nvis = pos0 + bt % T + 1;
@@ -1360,7 +1386,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_cand(const _Float16* __rest
     constexpr int WPT = MAXC / 32 / kSelThreads;   // bitmap words per thread
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t s_wave[kSelThreads / 64];
-    __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_pick[3];
     __shared__ uint32_t s_red[8];
     __shared__ uint32_t bm[MAXC / 32];
     const int bt = blockIdx.x, tid = threadIdx.x;
