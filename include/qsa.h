@@ -399,15 +399,18 @@ QSA_API int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc
  * tokens, then qsa_index_topk, qsa_attend and qsa_merge_gated, each reading
  * what the one before wrote.
  *
- * Every dependent kernel launch costs a few microseconds of idle GPU (the
- * end of one kernel and the start of the next), so the step folds calls
- * together where one workgroup already owns everything a call needs:
+ * Each call is its own kernel (or kernels), with its own ramp-up and drain,
+ * and data passed between calls goes through memory, so the step folds
+ * calls together where one workgroup already owns everything a call needs:
  *   - the append runs inside the index kernel when that kernel gives each
  *     problem one workgroup (one token per problem, batch >= 128, rows of
  *     at most 16384 cells, some token selecting): that workgroup writes its
  *     problem's new token, then scans the keys;
- *   - the merge and the gate run inside the attention kernel when P is 1,
- *     2 or 4 with the matrix kernel (as qsa_attend_merge).
+ *   - the merge and the gate run inside the attention kernel with the
+ *     matrix kernel when P is 1, 2 or 4 (as qsa_attend_merge), and when P
+ *     is a multiple of 4 above 4 with batch * T * Hkv >= 512 (the kernel then
+ *     gives each (token, KV head) one workgroup, which writes its chunks'
+ *     partials to the workspace and merges them itself).
  * Otherwise the calls run as their own kernels, in order.  The results
  * (new cache codes, scales and index keys; ids and n_sel; out) equal those
  * of the four calls with the same descriptors bit for bit.
@@ -421,8 +424,8 @@ QSA_API int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc
  * QSA_ERR_INVALID_ARG).  Ksc and Vsc must be 16-byte aligned.
  *
  * Workspace: at least qsa_step_workspace(idesc, adesc) bytes (the index
- * workspace, plus the partials when the merge runs as its own kernel),
- * 256-byte aligned, contents on entry irrelevant.
+ * workspace, plus room for the partials unless P is 1, 2 or 4 with the
+ * matrix kernel), 256-byte aligned, contents on entry irrelevant.
  * Supported: what each of the four calls supports.
  * --------------------------------------------------------------------- */
 QSA_API size_t qsa_step_workspace(const qsa_index_desc* idesc, const qsa_attn_desc* adesc);
