@@ -13,8 +13,8 @@ The default workload is the decode step (1 token, 24 x 256 query heads,
 independent caches, so the working set (~2.7 GB) is far larger than the
 256 MB last-level cache and every step streams from HBM.
 
-Timing: after the W warm-up steps, untimed steps continue until about 0.1 s
-of GPU time has passed (this GPU's clocks settle under a sustained HBM load
+Timing: after the W warm-up steps (and the probes), untimed steps continue
+until about 0.2 s of GPU time has passed (this GPU's clocks settle under a sustained HBM load
 only after some tens of milliseconds).  The K timed steps then run back to
 back between two HIP events on the launch stream (nothing else is enqueued
 between them); four more such blocks give the median/min/max over rounds.  A separate pass of the same
@@ -526,7 +526,6 @@ def main() -> None:
     for _ in range(W):
         step()
     torch.cuda.synchronize()
-    warm_up_to_steady_clocks(step, stream)
     n_sel_total = int(path.n_sel.sum().item())
     by = algorithmic_bytes(inp, B, n_sel_total)
     fused_att_bytes = by["attend"] + (by["out"] if fused else 0)
@@ -556,7 +555,8 @@ def main() -> None:
     if not args.no_ceiling:
         ceiling = hbm_ceiling(inp, dev, path, B, P, fused_att_bytes,
                               kernel_ms(attend_call))
-        warm_up_to_steady_clocks(step, stream)
+    # Last before the timed steps: one continuous run of untimed steps.
+    warm_up_to_steady_clocks(step, stream, seconds=0.2)
 
     def timed_block():
         """K steps between two events on the launch stream (nothing else

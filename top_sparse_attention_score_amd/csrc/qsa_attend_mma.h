@@ -169,34 +169,8 @@ __device__ __forceinline__ void attend_mma_block(
         }
     }
 
-    int eq = 0;  // fp32 queries are split as q * 2^-eq (see the header)
-    if constexpr (SHQ) {
-        // Every wave of the block has the same token (P % 4 == 0 and the grid
-        // covers whole blocks of items); each builds some query blocks.
-        const int bt0 = (int)(MCH ? group : (group * kMmaWaves) / P);
-        const size_t prow0 = (size_t)bt0 * Hq + (size_t)g * G;
-        if constexpr (!QF16) {
-            float amax = 0.f;
-            for (int blk = wave; blk < NB; blk += kMmaWaves)
-                amax = fmaxf(amax, q_block_absmax<G, D>(q, prow0, hq, q4, blk));
-            amax = wave_max16x4(amax);
-            if (lane == 0)
-                s_qmax[wave] = amax;
-            __syncthreads();
-            amax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
-            eq = pow2_shift(amax, kQShiftLo);
-        }
-        for (int blk = wave; blk < NB; blk += kMmaWaves) {
-            half8_t hi, lo;
-            load_q_block<G, D, QF16>(q, prow0, hq, q4, blk, eq, hi, lo);
-            q_all[(QH * blk) * 64 + lane] = hi;
-            if constexpr (!QF16)
-                q_all[(QH * blk + 1) * 64 + lane] = lo;
-        }
-        __syncthreads();
-    }
     const bool live = item < (long long)BT * P;
-    if constexpr (!MERGE) {
+    if constexpr (!MERGE && !SHQ) {
         if (!live)
             return;
     }
@@ -224,6 +198,90 @@ __device__ __forceinline__ void attend_mma_block(
             *(float4*)(po + ((prow + h) * P + cc) * D + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
+
+    const char* Kb = (const char*)Kq + (long long)b * kq_bs + (long long)g * D + 8 * q4;
+    const char* Ksb = (const char*)Ksc + (long long)b * ksc_bs + (long long)g * NB * 2;
+    const char* Vb = (const char*)Vq + (long long)b * vq_bs + (long long)g * D + 16 * (lane >> 5);
+    const char* Vsb = (const char*)Vsc + (long long)b * vsc_bs + (long long)g * NB * 2;
+    const int32_t* idr = ids + (size_t)bt * cap;
+
+    // Tile cell ids: jv for the V copy (cell lane & 31), ja / jb for the K
+    // gathers (cells hq and 16 + hq).  Ids outside [0, N) are undefined
+    // input; clamping keeps every gather inside the cache.  Tail cells
+    // repeat the tile's first cell (their weights are zero).
+    const int cl = lane & 31;
+    auto tile_ids = [&](int t0, int nt, int& jv, int& ja, int& jb) {
+        jv = idr[t0 + (cl < nt ? cl : 0)];
+        ja = idr[t0 + (hq < nt ? hq : 0)];
+        jb = idr[t0 + (16 + hq < nt ? 16 + hq : 0)];
+    };
+    auto clampN = [&](int j) { return (int)min((unsigned)j, (unsigned)(N - 1)); };
+
+    uint2 kc[2][NB];
+    uint32_t ksw[2][NPR];
+    auto load_k = [&](int ja, int jb) {
+        const char* kr[2] = {Kb + (long long)ja * kq_cs, Kb + (long long)jb * kq_cs};
+        const char* sr[2] = {Ksb + (long long)ja * ksc_cs, Ksb + (long long)jb * ksc_cs};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+                kc[hf][blk] = *(const uint2*)(kr[hf] + 32 * blk);
+            if constexpr (NPR == 4) {
+                const uint4 w = *(const uint4*)sr[hf];
+                ksw[hf][0] = w.x;
+                ksw[hf][1] = w.y;
+                ksw[hf][2] = w.z;
+                ksw[hf][3] = w.w;
+            } else {
+#pragma unroll
+                for (int w = 0; w < NPR; ++w)
+                    ksw[hf][w] = ((const uint32_t*)sr[hf])[w];
+            }
+        }
+    };
+
+    // The first tile's ids and K gathers go out now, so that their latency
+    // overlaps the query build below.
+    int t0 = beg;
+    int nt = min(TC, end - t0);
+    int jv = 0, ja = 0, jb = 0;
+    if (beg < end) {
+        tile_ids(t0, nt, jv, ja, jb);
+        jv = clampN(jv);
+        load_k(clampN(ja), clampN(jb));
+    }
+
+    int eq = 0;  // fp32 queries are split as q * 2^-eq (see the header)
+    if constexpr (SHQ) {
+        // Every wave of the block has the same token (P % 4 == 0 and the grid
+        // covers whole blocks of items); each builds some query blocks.
+        const int bt0 = (int)(MCH ? group : (group * kMmaWaves) / P);
+        const size_t prow0 = (size_t)bt0 * Hq + (size_t)g * G;
+        if constexpr (!QF16) {
+            float amax = 0.f;
+            for (int blk = wave; blk < NB; blk += kMmaWaves)
+                amax = fmaxf(amax, q_block_absmax<G, D>(q, prow0, hq, q4, blk));
+            amax = wave_max16x4(amax);
+            if (lane == 0)
+                s_qmax[wave] = amax;
+            __syncthreads();
+            amax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
+            eq = pow2_shift(amax, kQShiftLo);
+        }
+        for (int blk = wave; blk < NB; blk += kMmaWaves) {
+            half8_t hi, lo;
+            load_q_block<G, D, QF16>(q, prow0, hq, q4, blk, eq, hi, lo);
+            q_all[(QH * blk) * 64 + lane] = hi;
+            if constexpr (!QF16)
+                q_all[(QH * blk + 1) * 64 + lane] = lo;
+        }
+        __syncthreads();
+    }
+    if constexpr (!MERGE && SHQ) {
+        if (!live)
+            return;
+    }
     if (!MERGE && !MCH && beg >= end) {
         write_empty(c);
         return;
@@ -283,56 +341,6 @@ __device__ __forceinline__ void attend_mma_block(
             load_q_block<G, D, QF16>(q, prow, hq, q4, blk, eq, qh[blk], ql[blk]);
     }
     const float scale_q = __builtin_amdgcn_ldexpf(scale, eq);  // logit scale of the split query
-
-    const char* Kb = (const char*)Kq + (long long)b * kq_bs + (long long)g * D + 8 * q4;
-    const char* Ksb = (const char*)Ksc + (long long)b * ksc_bs + (long long)g * NB * 2;
-    const char* Vb = (const char*)Vq + (long long)b * vq_bs + (long long)g * D + 16 * (lane >> 5);
-    const char* Vsb = (const char*)Vsc + (long long)b * vsc_bs + (long long)g * NB * 2;
-    const int32_t* idr = ids + (size_t)bt * cap;
-
-    // Tile cell ids: jv for the V copy (cell lane & 31), ja / jb for the K
-    // gathers (cells hq and 16 + hq).  Ids outside [0, N) are undefined
-    // input; clamping keeps every gather inside the cache.  Tail cells
-    // repeat the tile's first cell (their weights are zero).
-    const int cl = lane & 31;
-    auto tile_ids = [&](int t0, int nt, int& jv, int& ja, int& jb) {
-        jv = idr[t0 + (cl < nt ? cl : 0)];
-        ja = idr[t0 + (hq < nt ? hq : 0)];
-        jb = idr[t0 + (16 + hq < nt ? 16 + hq : 0)];
-    };
-    auto clampN = [&](int j) { return (int)min((unsigned)j, (unsigned)(N - 1)); };
-
-    uint2 kc[2][NB];
-    uint32_t ksw[2][NPR];
-    auto load_k = [&](int ja, int jb) {
-        const char* kr[2] = {Kb + (long long)ja * kq_cs, Kb + (long long)jb * kq_cs};
-        const char* sr[2] = {Ksb + (long long)ja * ksc_cs, Ksb + (long long)jb * ksc_cs};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk)
-                kc[hf][blk] = *(const uint2*)(kr[hf] + 32 * blk);
-            if constexpr (NPR == 4) {
-                const uint4 w = *(const uint4*)sr[hf];
-                ksw[hf][0] = w.x;
-                ksw[hf][1] = w.y;
-                ksw[hf][2] = w.z;
-                ksw[hf][3] = w.w;
-            } else {
-#pragma unroll
-                for (int w = 0; w < NPR; ++w)
-                    ksw[hf][w] = ((const uint32_t*)sr[hf])[w];
-            }
-        }
-    };
-
-    int t0 = beg;
-    int nt = min(TC, end - t0);
-    int jv, ja, jb;
-    tile_ids(t0, nt, jv, ja, jb);
-    jv = clampN(jv);
-    load_k(clampN(ja), clampN(jb));
-
     // Transpose-read base of this lane: cell 8*q4 + hq/2 of the [chunk][cell]
     // table, 8-byte half hq&1; slice t adds 512*t.
     const int8_t* v_rd = v_s + 16 * (8 * q4 + (hq >> 1)) + 8 * (hq & 1);
