@@ -265,10 +265,74 @@ static int gpu_run(const char* dir)
     void* h_ids = malloc(nids);
     void* h_ns = malloc((size_t)B * T * 4);
     void* h_out = malloc(nq);
-    CHECK(h_ids && h_ns && h_out, "host buffers");
+    void* h_tmp = malloc(nq > nids ? nq : nids);
+    CHECK(h_ids && h_ns && h_out && h_tmp, "host buffers");
     CHECK(hipMemcpy(h_ids, ids, nids, hipMemcpyDeviceToHost) == hipSuccess, "ids back");
     CHECK(hipMemcpy(h_ns, n_sel, (size_t)B * T * 4, hipMemcpyDeviceToHost) == hipSuccess, "n_sel");
     CHECK(hipMemcpy(h_out, out, nq, hipMemcpyDeviceToHost) == hipSuccess, "out back");
+
+    /* qsa_attend_merge on the same ids: the output of the two calls, bit for
+     * bit (when the split fits one workgroup). */
+    if (P == 1 || P == 2 || P == 4) {
+        void* out2 = to_device(NULL, nq);
+        CHECK(out2 != NULL, "device buffer");
+        st = qsa_attend_merge(&at, dev[2], dev[3], dev[4], dev[5], dev[6], ids, n_sel, dev[10],
+                              out2, NULL);
+        CHECK(st == QSA_OK, "qsa_attend_merge: %s", qsa_status_string(st));
+        CHECK(hipMemcpy(h_tmp, out2, nq, hipMemcpyDeviceToHost) == hipSuccess, "out2 back");
+        CHECK(memcmp(h_tmp, h_out, nq) == 0, "qsa_attend_merge differs from attend + merge");
+        hipFree(out2);
+        printf("attend_merge equal\n");
+    }
+
+    /* qsa_step from the original inputs: cache, ids, n_sel and output equal
+     * to the four calls above, bit for bit. */
+    {
+        void* sdev[7];
+        for (int i = 0; i < 7; ++i) {
+            void* orig = read_file(dir, names[i], sizes[i]);
+            CHECK(orig != NULL, "input %s", names[i]);
+            sdev[i] = to_device(orig, sizes[i]);
+            CHECK(sdev[i] != NULL, "device copy of %s", names[i]);
+            free(orig);
+        }
+        const size_t sws_bytes = qsa_step_workspace(&id, &at);
+        CHECK(sws_bytes > 0, "step workspace size");
+        void* sws = to_device(NULL, sws_bytes);
+        void* sids = to_device(NULL, nids);
+        void* sns = to_device(NULL, (size_t)B * T * 4);
+        void* sout = to_device(NULL, nq);
+        CHECK(sws && sids && sns && sout, "device buffers");
+        st = qsa_step(&ad, &id, &at, dev[7], dev[8], dev[9], sdev[3], sdev[4], sdev[5], sdev[6],
+                      sdev[1], sdev[0], sdev[2], dev[10], sids, sns, sout, sws, sws_bytes, NULL);
+        CHECK(st == QSA_OK, "qsa_step: %s", qsa_status_string(st));
+        CHECK(hipMemcpy(h_tmp, sout, nq, hipMemcpyDeviceToHost) == hipSuccess, "step out");
+        CHECK(memcmp(h_tmp, h_out, nq) == 0, "qsa_step output differs");
+        CHECK(hipMemcpy(h_tmp, sids, nids, hipMemcpyDeviceToHost) == hipSuccess, "step ids");
+        CHECK(memcmp(h_tmp, h_ids, nids) == 0, "qsa_step ids differ");
+        CHECK(hipMemcpy(h_tmp, sns, (size_t)B * T * 4, hipMemcpyDeviceToHost) == hipSuccess,
+              "step n_sel");
+        CHECK(memcmp(h_tmp, h_ns, (size_t)B * T * 4) == 0, "qsa_step n_sel differs");
+        for (int i = 1; i <= 6; ++i) {
+            if (i == 2)
+                continue;
+            void* a = malloc(sizes[i]);
+            void* b = malloc(sizes[i]);
+            CHECK(a && b, "host buffers");
+            CHECK(hipMemcpy(a, sdev[i], sizes[i], hipMemcpyDeviceToHost) == hipSuccess, "cache");
+            CHECK(hipMemcpy(b, dev[i], sizes[i], hipMemcpyDeviceToHost) == hipSuccess, "cache");
+            CHECK(memcmp(a, b, sizes[i]) == 0, "qsa_step cache %s differs", names[i]);
+            free(a);
+            free(b);
+        }
+        for (int i = 0; i < 7; ++i)
+            hipFree(sdev[i]);
+        hipFree(sws);
+        hipFree(sids);
+        hipFree(sns);
+        hipFree(sout);
+        printf("step equal\n");
+    }
     CHECK(write_file(dir, "ids.out", h_ids, nids) == 0, "write ids");
     CHECK(write_file(dir, "n_sel.out", h_ns, (size_t)B * T * 4) == 0, "write n_sel");
     CHECK(write_file(dir, "out.out", h_out, nq) == 0, "write out");
@@ -290,6 +354,7 @@ static int gpu_run(const char* dir)
     free(h_ids);
     free(h_ns);
     free(h_out);
+    free(h_tmp);
     printf("gpu run ok\n");
     return 0;
 }

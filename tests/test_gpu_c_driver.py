@@ -4,7 +4,9 @@ qsa_kv_append -> qsa_index_topk -> qsa_attend -> qsa_merge_gated through
 include/qsa.h on the default stream with the library's default softmax
 scale, and writes the results back.  The oracle checks them: appended codes,
 scales and index keys and the kept ids bit for bit, the gated output within
-max-abs 2e-3 / rel-L2 1e-2."""
+max-abs 2e-3 / rel-L2 1e-2.  The same program also runs qsa_attend_merge on
+the same ids and qsa_step from the original inputs and checks, in C, that
+they give the four calls' results bit for bit."""
 import math
 import os
 import subprocess
@@ -50,7 +52,8 @@ def test_c_driver_whole_path(orc, tmp_path, cfg, batch):
     r = subprocess.run([ABI_DRIVER, "run", str(tmp_path)], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert "gpu run ok" in r.stdout
+    assert "gpu run ok" in r.stdout and "step equal" in r.stdout
+    assert ("attend_merge equal" in r.stdout) == (inp["P"] in (1, 2, 4))
 
     rK, rKs, rV, rVs, rI = orc.kv_append(k_new, v_new, i_new, inp["Kq"], inp["Ksc"], inp["Vq"],
                                          inp["Vsc"], inp["K_idx"], pos0=pos0)

@@ -6,9 +6,10 @@ scales, index keys), ids, n_sel and the output must be equal bit for bit.
 The cases cover each way the step folds calls: the append inside the
 decode scan/select kernel (one token, 128 or more problems, rows of at most
 16384 cells) or as its own kernel; the merge inside the attention kernel
-(P in {1, 2, 4}) or as its own kernel; dense rows; the draft, long and
-prompt-chunk index paths; fp16 queries and outputs; no index keys appended.
-Two cases are also checked against the oracle."""
+(P in {1, 2, 4}; P a multiple of 4 with 512 or more (token, KV head) pairs)
+or as its own kernel (other splits, the vector kernel); dense rows; the
+draft, long and prompt-chunk index paths; fp16 queries and outputs; no index
+keys appended.  Two cases are also checked against the oracle."""
 import math
 
 import numpy as np
@@ -48,12 +49,15 @@ CASES = [
     ("long", 1, 64, True, True, dict(pos0=100000)),
     ("prompt_small", 1, 1, True, True, {}),
     ("prompt_small", 1, 4, False, True, {}),
+    ("decode", 3, 4, True, True, dict(algo=qsa.QSA_ATTEND_VECTOR)),   # vector kernel: merge apart
+    ("decode", 128, 8, True, True, dict(tile=4, algo=qsa.QSA_ATTEND_VECTOR)),
 ]
 
 
 def _inputs(cfg, seed, B, over):
     over = dict(over)
     tile = over.pop("tile", None)
+    over.pop("algo", None)
     c = PROMPT_SMALL if cfg == "prompt_small" else cfg
     if tile is None:
         return make_inputs(c, seed=seed, batch=B, **over)
@@ -83,11 +87,11 @@ def _pdesc(inp):
                            Hkv=inp["Hkv"], D=inp["D"], d_idx=inp["di"])
 
 
-def _separate(inp, dev, P, rows):
+def _separate(inp, dev, P, rows, algo=qsa.QSA_ATTEND_AUTO):
     k_new, v_new, i_new, gate = rows
     qsa.qsa_kv_append(_pdesc(inp), k_new, v_new, i_new, dev["Kq"], dev["Ksc"], dev["Vq"],
                       dev["Vsc"], dev["K_idx"])
-    path = qsa.path_for(inp, P=P)
+    path = qsa.path_for(inp, P=P, algo=algo)
     path.run(dict(dev, gate=gate))
     return path
 
@@ -125,7 +129,7 @@ def test_step_equals_separate_calls(case):
     dev_a = qsa.to_device(inp)
     dev_b = {k: v.clone() for k, v in dev_a.items()}
     rows = _new_rows(inp, 41 + B, with_idx, with_gate)
-    path = _separate(inp, dev_a, P, rows)
+    path = _separate(inp, dev_a, P, rows, over.get("algo", qsa.QSA_ATTEND_AUTO))
     ids, n_sel, out, ws = _step(inp, dev_b, path, rows)
     torch.cuda.synchronize()
     for name in ("Kq", "Ksc", "Vq", "Vsc", "K_idx"):
