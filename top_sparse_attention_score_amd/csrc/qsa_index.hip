@@ -1047,15 +1047,19 @@ __global__ __launch_bounds__(256) void k_idx_sample(const _Float16* __restrict__
         for (int st = 0; st < KS; ++st)
             qt[i][st] = *(const h8_t*)(src + kperm(st, grp));
     }
-#pragma unroll 1
+    h8_t kc4[4][KS];   // all four groups' keys in flight together
+#pragma unroll
     for (int g16 = 0; g16 < 4; ++g16) {
-        const int s0 = s_base + 16 * g16;
-        const int cell = sample_cell(s0 + r, span);
+        const int cell = sample_cell(s_base + 16 * g16 + r, span);
         const _Float16* src = K_idx + ((size_t)b * N + cell) * DI;
-        h8_t kc[KS];
 #pragma unroll
         for (int st = 0; st < KS; ++st)
-            kc[st] = *(const h8_t*)(src + kperm(st, grp));
+            kc4[g16][st] = *(const h8_t*)(src + kperm(st, grp));
+    }
+#pragma unroll
+    for (int g16 = 0; g16 < 4; ++g16) {
+        const int s0 = s_base + 16 * g16;
+        const h8_t (&kc)[KS] = kc4[g16];
         int ce[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -1077,48 +1081,121 @@ __global__ __launch_bounds__(256) void k_idx_sample(const _Float16* __restrict__
     }
 }
 
-// One workgroup per token: the candidate bound from the token's sample keys.
-__global__ __launch_bounds__(kSelThreads) void k_sel_thresh(const uint32_t* __restrict__ samp,
-                                                            uint32_t* __restrict__ thr,
-                                                            uint32_t* __restrict__ gcount, int T,
-                                                            int pos0, int k, int dense_max)
+// Number of keys of the wave at or above t: K keys per lane, 0 = absent.
+template <int K>
+__device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&v)[K], uint32_t t)
 {
-    constexpr int M = kSampleCells / kSelThreads;
-    __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t s_wave[kSelThreads / 64];
-    __shared__ uint32_t s_pick[3];
-    __shared__ uint32_t s_red[8];
-    const int bt = blockIdx.x;
+    uint32_t n = 0;
+#pragma unroll
+    for (int m = 0; m < K; ++m)
+        n += (uint32_t)__popcll(__ballot(v[m] >= t));
+    return n;
+}
+
+// The r-th largest key of the wave (r >= 1, at most the number of nonzero
+// keys), given that it lies in [lo, hi] (lo >= 1): the largest t with at
+// least r keys >= t, built bit by bit below the bits that lo and hi share,
+// each trial value kept when the wave-wide count still reaches r.
+template <int K>
+__device__ __forceinline__ uint32_t wave_kth_in(const uint32_t (&v)[K], uint32_t r, uint32_t lo,
+                                                uint32_t hi)
+{
+    const uint32_t diff = lo ^ hi;
+    if (diff == 0u)
+        return lo;
+    const int nb = 32 - __clz(diff);
+    uint32_t t = lo & ~((nb == 32 ? 0u : (1u << nb)) - 1u);
+#pragma unroll 1
+    for (int bit = nb - 1; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        if (wave_count_ge(v, c) >= r)
+            t = c;
+    }
+    return t;
+}
+
+// One wave per token: the candidate bound from the token's sample keys, 32
+// per lane in registers.  The r-th largest key x is found in three stages:
+//   1. each lane's two largest keys; the r-th largest of these 128 values,
+//      L, is at most x (they are a subset of the keys);
+//   2. the keys >= L (all keys >= x among them: about r plus a few dozen
+//      for evenly spread samples) are compacted into LDS;
+//   3. the exact r-th largest of those, at most four per lane, bit by bit.
+// When L is 0 (r above the number of nonzero top-two values) or more than
+// 256 keys reach it, stage 3 runs on all 32 keys per lane instead.  Absent
+// samples (key 0) never count, since every trial value is nonzero.
+__global__ __launch_bounds__(64) void k_sel_thresh(const uint32_t* __restrict__ samp,
+                                                   uint32_t* __restrict__ thr,
+                                                   uint32_t* __restrict__ gcount, int T, int pos0,
+                                                   int k, int dense_max)
+{
+    constexpr int M = kSampleCells / 64;
+    constexpr int C = 4;   // compacted keys per lane
+    __shared__ uint32_t s_k[64 * C];
+    const int bt = blockIdx.x, lane = threadIdx.x;
     const int nvis = pos0 + bt % T + 1;
     if (!token_selects(nvis, k, dense_max)) {
-        if (threadIdx.x == 0) {
+        if (lane == 0) {
             thr[bt] = 0xffffffffu;   // above every score key: no candidates
             gcount[bt] = 0u;
         }
         return;
     }
-    const uint32_t* row = samp + (size_t)bt * kSampleCells;
+    const uint4* row = (const uint4*)(samp + (size_t)bt * kSampleCells);
     uint32_t v[M];
-    uint32_t nv = 0;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        v[m] = row[m * kSelThreads + threadIdx.x];
-        nv += v[m] != 0u ? 1u : 0u;
+    for (int m = 0; m < M / 4; ++m) {
+        const uint4 x = row[m * 64 + lane];
+        v[4 * m] = x.x;
+        v[4 * m + 1] = x.y;
+        v[4 * m + 2] = x.z;
+        v[4 * m + 3] = x.w;
     }
-    uint32_t total;
-    block_excl_scan(nv, total, s_wave);
-    const float mu = (float)k * (float)total / (float)nvis;
-    uint32_t r = (uint32_t)ceilf(mu + 4.f * sqrtf(mu) + 4.f);
-    uint32_t bound = 0u;   // 0: every visible cell is a candidate
-    if (r < total)
-        bound = wg_kth_largest(
-            [&](auto f) {
+    uint32_t total = 0;
 #pragma unroll
-                for (int m = 0; m < M; ++m)
-                    f(v[m]);
-            },
-            r, hist, s_red, s_wave, s_pick);
-    if (threadIdx.x == 0) {
+    for (int m = 0; m < M; ++m)
+        total += (uint32_t)__popcll(__ballot(v[m] != 0u));
+    const float mu = (float)k * (float)total / (float)nvis;
+    const uint32_t r = (uint32_t)ceilf(mu + 4.f * sqrtf(mu) + 4.f);
+    uint32_t bound = 0u;   // 0: every visible cell is a candidate
+    if (r < total) {
+        uint32_t top[2] = {0u, 0u};   // this lane's two largest keys
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            top[1] = max(top[1], min(top[0], v[m]));
+            top[0] = max(top[0], v[m]);
+        }
+        uint32_t hi = top[0];   // the wave's largest key
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+        const uint32_t L = wave_count_ge(top, 1u) >= r ? wave_kth_in(top, r, 1u, hi) : 0u;
+        uint32_t n = 0;   // keys >= L, compacted in order of (register, lane)
+        if (L != 0u) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const bool in = v[m] >= L;
+                const unsigned long long bal = __ballot(in);
+                const uint32_t pos = n + __builtin_amdgcn_mbcnt_hi(
+                                             (uint32_t)(bal >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                if (in && pos < (uint32_t)(64 * C))
+                    s_k[pos] = v[m];
+                n += (uint32_t)__popcll(bal);
+            }
+        }
+        if (L != 0u && n <= (uint32_t)(64 * C)) {
+            __syncthreads();
+            uint32_t c[C];
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+                c[j] = (uint32_t)(j * 64 + lane) < n ? s_k[j * 64 + lane] : 0u;
+            bound = wave_kth_in(c, r, L, hi);
+        } else {
+            bound = wave_kth_in(v, r, 1u, hi);
+        }
+    }
+    if (lane == 0) {
         thr[bt] = bound;
         gcount[bt] = 0u;
     }
@@ -1132,7 +1209,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sel_thresh(const uint32_t* __re
 // a wave walks 256 cells, 32 per step, with the next step's keys in flight,
 // and keeps the (score, cell) pairs at or above each token's bound.
 template <int DI>
-__global__ __launch_bounds__(256) void k_idx_collect(const _Float16* __restrict__ q_idx,
+__global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restrict__ q_idx,
                                                      const _Float16* __restrict__ K_idx,
                                                      const uint32_t* __restrict__ thr,
                                                      uint32_t* __restrict__ gcount,
@@ -1192,6 +1269,9 @@ __global__ __launch_bounds__(256) void k_idx_collect(const _Float16* __restrict_
     // instructions pipeline), then the keys of step cb + 1 into the same
     // registers, then the candidates while those are in flight.
     auto step = [&](int cb, h8_t (&kc)[2][KS]) {
+        // The query operands are read from LDS at every step rather than
+        // held in 16 KS registers across the loop (three waves per SIMD).
+        __asm__ volatile("" ::: "memory");
         float4_t acc[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1702,8 +1782,7 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLa
         const _Float16* K = (const _Float16*)a.K_idx;
 #define QSA_FUSED(DI)                                                                          \
     k_idx_sample<DI><<<gs, 256, 0, s>>>(q, K, w.samp, a.T, a.N, a.pos0, nvis_max);             \
-    k_sel_thresh<<<BT, kSelThreads, 0, s>>>(w.samp, w.thr, w.gcount, a.T, a.pos0, a.k,          \
-                                            a.dense_max);                                     \
+    k_sel_thresh<<<BT, 64, 0, s>>>(w.samp, w.thr, w.gcount, a.T, a.pos0, a.k, a.dense_max);   \
     k_idx_collect<DI><<<gc, 256, 0, s>>>(q, K, w.thr, w.gcount, w.fcand, a.T, a.N, a.pos0, n_cr, \
                                          n_tb, a.B);                                          \
     k_sel_cand<DI, kFusedMaxCells, false><<<BT, kSelThreads, 0, s>>>(                          \
@@ -1728,8 +1807,7 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLa
         const _Float16* K = (const _Float16*)a.K_idx;
 #define QSA_LONG1(DI)                                                                          \
     k_idx_sample<DI><<<gs, 256, 0, s>>>(q, K, w.samp, 1, a.N, a.pos0, nvis_max);               \
-    k_sel_thresh<<<a.B, kSelThreads, 0, s>>>(w.samp, w.thr, w.gcount, 1, a.pos0, a.k,           \
-                                             a.dense_max);                                    \
+    k_sel_thresh<<<a.B, 64, 0, s>>>(w.samp, w.thr, w.gcount, 1, a.pos0, a.k, a.dense_max);    \
     k_scan_collect<DI><<<dim3((nvis_max + idx_scan_rows_per_block<DI>() * kScanCollectSpan -   \
                                1) / (idx_scan_rows_per_block<DI>() * kScanCollectSpan),       \
                               a.B),                                                            \
