@@ -52,8 +52,13 @@ def _oracle_ids(orc, inp, slice_tokens=8):
     return ids, ns
 
 
+# Many tokens (four 16-token column blocks per workgroup) and 2-16 tokens
+# (one column block: the draft's shape), with ragged last blocks.
 @pytest.mark.parametrize("N,T,pos0,batch", [(65536, 256, 65280, 1), (65536, 128, 30000, 2),
-                                            (40000, 200, 39800, 1), (16384, 64, 16320, 2)])
+                                            (40000, 200, 39800, 1), (16384, 64, 16320, 2),
+                                            (65536, 8, 65528, 2), (65536, 16, 60000, 1),
+                                            (65536, 17, 65000, 1), (30000, 5, 29990, 3),
+                                            (16384, 2, 16382, 2)])
 def test_fused_index_matches_oracle(orc, N, T, pos0, batch):
     inp = make_inputs("prompt", seed=9300 + T, batch=batch, N=N, T=T, pos0=pos0)
     say(f"[fused index] N={N} T={T} pos0={pos0} B={batch}")
@@ -71,21 +76,24 @@ def _sample_cells(span: int, n: int = 2048) -> np.ndarray:
     return (s * stride + off).astype(np.int64)
 
 
-def test_fused_index_fallbacks(orc):
-    """Problem 0: tokens 0-15 have a zero index query (every score equal),
-    tokens 16-31 see scores from two values (half the row ties at the top):
-    their candidate lists overflow.  Problem 1: 1000 sampled cells are
-    planted above all others, so the sampled bound keeps fewer than k
-    candidates.  Problem 2: four score values, a large exact tie at the k-th
-    inside the candidate list.  Tokens 32-63 of problem 0 take the normal
-    path."""
-    N, T = 65536, 64
+@pytest.mark.parametrize("T", [64, 8])
+def test_fused_index_fallbacks(orc, T):
+    """Problem 0: the first quarter of the tokens have a zero index query
+    (every score equal), the second quarter see scores from two values (half
+    the row ties at the top): their candidate lists overflow.  Problem 1:
+    1000 sampled cells are planted above all others, so the sampled bound
+    keeps fewer than k candidates.  Problem 2: four score values, a large
+    exact tie at the k-th inside the candidate list.  The other half of
+    problem 0's tokens take the normal path.  T = 64 runs four column blocks
+    per workgroup, T = 8 one."""
+    N = 65536
     pos0 = N - T
-    inp = make_inputs("prompt", seed=9400, batch=3, N=N, T=T, pos0=pos0)
-    inp["q_idx"][0, :16] = 0
+    q1, q2 = T // 4, T // 2
+    inp = make_inputs("prompt", seed=9400 + T, batch=3, N=N, T=T, pos0=pos0)
+    inp["q_idx"][0, :q1] = 0
     rng = np.random.default_rng(9401)
-    inp["q_idx"][0, 16:32] = 0
-    inp["q_idx"][0, 16:32, 0] = 1.0
+    inp["q_idx"][0, q1:q2] = 0
+    inp["q_idx"][0, q1:q2, 0] = 1.0
     inp["K_idx"][0, :, 0] = np.where(rng.random(N) < 0.5, 1.0, 0.0).astype(np.float16)
     cells = _sample_cells(pos0 + T)
     assert len(np.unique(cells)) == 2048 and cells[:1000].max() <= pos0

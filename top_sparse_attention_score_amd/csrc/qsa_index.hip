@@ -13,14 +13,15 @@
 //                row once, 16 lanes per row (coalesced), scores it with
 //                v_dot2 (fp16 x fp16 products, fp32 accumulation) and sums
 //                the row across its lanes with DPP.
-//   k_idx_mscan  2 <= T <= 16 (draft): the same stream, scored on MFMA
+//   k_idx_mscan  2 <= T <= 16 outside the fused path's range (rows under
+//                16384 or over 65536 cells): the same stream, scored on MFMA
 //                (v_mfma_f32_16x16x32_f16, tokens padded to 16 rows), no
 //                cross-lane reduction.
 //   k_scan_select one token with a row of at most 16384 cells (decode):
 //                scan and select fused in one workgroup per token.
 //   k_idx_sample, k_sel_thresh, k_idx_collect, k_sel_cand
-//                many tokens (T > 16, e.g. a prompt chunk) against rows of
-//                16384 to 65536 cells: the score GEMM on MFMA keeps only the
+//                two or more tokens (a draft batch, a prompt chunk) against
+//                rows of 16384 to 65536 cells: the score GEMM on MFMA keeps only the
 //                cells at or above a sampled bound, then an exact select
 //                among them; the score matrix is never written (see the
 //                section "many tokens: fused select").
@@ -942,8 +943,8 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
 
 // ------------------------------------------ many tokens: fused select ---
 //
-// For many tokens (T > 16) against rows of up to kFusedMaxCells cells the
-// score matrix is never written.  Four kernels:
+// For two or more tokens against rows of kFusedMinCells to kFusedMaxCells
+// cells the score matrix is never written.  Four kernels:
 //   k_idx_sample   scores a fixed sample of kSampleCells cells of the row
 //                  (evenly spread, each at a hashed offset inside its stride)
 //                  for every token and writes their keys (0 where the token
@@ -978,6 +979,7 @@ constexpr int kCandCap = 8192;        // candidates kept per token
 constexpr int kCollectList = 64;      // LDS candidate slots per (workgroup, token)
 constexpr int kFusedMaxCells = 65536; // longest row of the fused path (bitmap, registers)
 constexpr int kFusedMinCells = 16384; // shorter rows write their keys instead
+constexpr int kFusedMinTokens = 2;    // fewer tokens per problem take the one-token paths
 // One-token rows between the register select's limit and this length take
 // the sampled-bound path with k_scan_collect (bitmap of the row in LDS).
 constexpr int kLongFusedMaxCells = 262144;
@@ -1205,10 +1207,11 @@ __global__ __launch_bounds__(64) void k_sel_thresh(const uint32_t* __restrict__ 
 // arranged so that the workgroups of one cell range run on one XCD one
 // after another (dispatch goes round-robin over the 8 XCDs): the range's
 // keys stay in that XCD's L2 for all its token blocks.  The four waves share
-// 64 tokens (four 16-token column blocks), whose query operands sit in LDS;
-// a wave walks 256 cells, 32 per step, with the next step's keys in flight,
-// and keeps the (score, cell) pairs at or above each token's bound.
-template <int DI>
+// 16 NCB tokens (NCB 16-token column blocks: 4, or 1 when a problem has at
+// most 16 tokens), whose query operands sit in LDS; a wave walks 256 cells,
+// 32 per step, with the next step's keys in flight, and keeps the (score,
+// cell) pairs at or above each token's bound.
+template <int DI, int NCB>
 __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restrict__ q_idx,
                                                      const _Float16* __restrict__ K_idx,
                                                      const uint32_t* __restrict__ thr,
@@ -1219,11 +1222,11 @@ __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restri
     constexpr int KS = DI / 32;
     // Row pitch kCollectList + 1 entries, so the lists of the 16 tokens that
     // one instruction appends to start on different LDS banks.
-    __shared__ uint2 lst[64][kCollectList + 1];
-    __shared__ uint32_t cnt[64];
+    __shared__ uint2 lst[16 * NCB][kCollectList + 1];
+    __shared__ uint32_t cnt[16 * NCB];
     // Query operands: slot (i, st) holds, for lane (r, g), token 16 i + r,
     // elements kperm(st, g): one 16-byte slot per lane, lanes contiguous.
-    __shared__ h8_t qs[4][KS][64];
+    __shared__ h8_t qs[NCB][KS][64];
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     const int tb = local % n_tb;
     const int crb = (local / n_tb) * 8 + xcd;     // (problem, cell range) index
@@ -1232,23 +1235,23 @@ __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restri
     const int b = crb / n_cr, cr = crb % n_cr;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, grp = lane >> 4;
-    const int tok0 = tb * 64;
+    const int tok0 = tb * 16 * NCB;
     const int cell_base = cr * 1024 + w * 256;
-    const int nvis_hi = pos0 + min(tok0 + 64, T);   // cells seen by the block's last token
+    const int nvis_hi = pos0 + min(tok0 + 16 * NCB, T);   // cells seen by the block's last token
     const int nvis_lo = pos0 + tok0 + 1;             // cells seen by its first token
-    if (threadIdx.x < 64)
+    if (threadIdx.x < 16 * NCB)
         cnt[threadIdx.x] = 0u;
-    {   // wave w fills column block w of the query operands
+    if (w < NCB) {   // wave w fills column block w of the query operands
         const int tok = min(tok0 + 16 * w + r, T - 1);
         const _Float16* src = q_idx + ((size_t)b * T + tok) * DI;
 #pragma unroll
         for (int st = 0; st < KS; ++st)
             qs[w][st][lane] = *(const h8_t*)(src + kperm(st, grp));
     }
-    float thf[4];   // score bound of the lane's token in each column block
-    int nv[4];
+    float thf[NCB];   // score bound of the lane's token in each column block
+    int nv[NCB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NCB; ++i) {
         const int tok = tok0 + 16 * i + r;
         thf[i] = key_to_score(tok < T ? thr[(size_t)b * T + tok] : 0xffffffffu);
         nv[i] = pos0 + tok + 1;
@@ -1272,9 +1275,9 @@ __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restri
         // The query operands are read from LDS at every step rather than
         // held in 16 KS registers across the loop (three waves per SIMD).
         __asm__ volatile("" ::: "memory");
-        float4_t acc[4][2];
+        float4_t acc[NCB][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NCB; ++i) {
             h8_t qv[KS];
 #pragma unroll
             for (int st = 0; st < KS; ++st)
@@ -1289,10 +1292,10 @@ __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restri
         // Candidate masks, bit 4*jj + e: cell c0 + 16 jj + 4 grp + e of the
         // lane's token in column block i (non-short-circuit tests, no
         // branches; visibility only where part of the step lies past a token).
-        uint32_t mk[4];
+        uint32_t mk[NCB];
         if (c0 + 32 <= nvis_lo) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NCB; ++i) {
                 mk[i] = 0u;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
@@ -1302,7 +1305,7 @@ __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restri
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NCB; ++i) {
                 mk[i] = 0u;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
@@ -1340,10 +1343,9 @@ __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restri
                 ++slot;
             }
         };
-        append(0, acc[0][0], acc[0][1], mk[0]);
-        append(1, acc[1][0], acc[1][1], mk[1]);
-        append(2, acc[2][0], acc[2][1], mk[2]);
-        append(3, acc[3][0], acc[3][1], mk[3]);
+#pragma unroll
+        for (int i = 0; i < NCB; ++i)
+            append(i, acc[i][0], acc[i][1], mk[i]);
     };
 
     h8_t kc[2][KS];
@@ -1356,6 +1358,8 @@ __global__ __launch_bounds__(256, 3) void k_idx_collect(const _Float16* __restri
     __syncthreads();
     // Flush: wave w appends the lists of tokens 16w .. 16w+15, reserving all
     // sixteen slot ranges at once (lane j for token 16w + j).
+    if (w >= NCB)
+        return;
     const int tl_l = 16 * w + (lane & 15);
     const int tok_l = tok0 + tl_l;
     const uint32_t n_l = (tok_l < T) ? min(cnt[tl_l], (uint32_t)kCollectList) : 0u;
@@ -1687,7 +1691,7 @@ static SelWs carve(void* ws, int B, int T, int N, size_t* total)
     w.cand = (uint32_t*)take(BT * kCap * 8);
     w.pivot = (uint32_t*)take(BT * 8);
     // fused many-token path (k_idx_sample .. k_sel_cand)
-    const bool fused = (T > 16 && N <= kFusedMaxCells) ||
+    const bool fused = (T >= kFusedMinTokens && N <= kFusedMaxCells) ||
                        (T == 1 && N > kRowThreads * 64 && N <= kLongFusedMaxCells);
     w.thr = (uint32_t*)take(fused ? BT * 4 : 0);
     w.gcount = (uint32_t*)take(fused ? BT * 4 : 0);
@@ -1772,19 +1776,24 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLa
         if (e != hipSuccess)
             return e;
     }
-    const bool fused = any_select && a.T > 16 && a.N <= kFusedMaxCells &&
+    const bool fused = any_select && a.T >= kFusedMinTokens && a.N <= kFusedMaxCells &&
                        nvis_max >= kFusedMinCells && a.k <= kCandCap / 2;
     if (fused) {
         const dim3 gs(kSampleCells / 256, (a.T + 63) / 64, a.B);
-        const int n_cr = (nvis_max + 1023) / 1024, n_tb = (a.T + 63) / 64;
+        const int ncb = a.T <= 16 ? 1 : 4;   // 16-token column blocks per workgroup
+        const int n_cr = (nvis_max + 1023) / 1024, n_tb = (a.T + 16 * ncb - 1) / (16 * ncb);
         const int gc = ((n_cr * a.B + 7) / 8) * 8 * n_tb;
         const _Float16* q = (const _Float16*)a.q_idx;
         const _Float16* K = (const _Float16*)a.K_idx;
 #define QSA_FUSED(DI)                                                                          \
     k_idx_sample<DI><<<gs, 256, 0, s>>>(q, K, w.samp, a.T, a.N, a.pos0, nvis_max);             \
     k_sel_thresh<<<BT, 64, 0, s>>>(w.samp, w.thr, w.gcount, a.T, a.pos0, a.k, a.dense_max);   \
-    k_idx_collect<DI><<<gc, 256, 0, s>>>(q, K, w.thr, w.gcount, w.fcand, a.T, a.N, a.pos0, n_cr, \
-                                         n_tb, a.B);                                          \
+    if (ncb == 1)                                                                              \
+        k_idx_collect<DI, 1><<<gc, 256, 0, s>>>(q, K, w.thr, w.gcount, w.fcand, a.T, a.N, a.pos0, \
+                                                n_cr, n_tb, a.B);                              \
+    else                                                                                       \
+        k_idx_collect<DI, 4><<<gc, 256, 0, s>>>(q, K, w.thr, w.gcount, w.fcand, a.T, a.N, a.pos0, \
+                                                n_cr, n_tb, a.B);                              \
     k_sel_cand<DI, kFusedMaxCells, false><<<BT, kSelThreads, 0, s>>>(                          \
         q, K, w.gcount, w.fcand, w.keys, a.ids, a.n_sel,                                      \
                                               a.T, a.N, a.pos0, a.k, a.dense_max, a.cap)
