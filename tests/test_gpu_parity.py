@@ -356,7 +356,7 @@ def test_chip_wide_select_ties(orc, case):
             assert np.array_equal(res["ids"][:, t, :2048], np.tile(np.arange(2048), (2, 1)))
 
 
-@pytest.mark.parametrize("cfg,batch", [("decode", 256), ("draft", 32), ("long", 16)])
+@pytest.mark.parametrize("cfg,batch", [("decode", 512), ("draft", 32), ("long", 16)])
 def test_bench_launch_configuration(orc, cfg, batch):
     """The batch sizes bench.py times, built the way it builds them (a few
     distinct seeded problems tiled over the batch): every replica's ids equal

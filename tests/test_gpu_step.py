@@ -77,7 +77,7 @@ def _new_rows(inp, seed, with_idx, with_gate):
     i_new = torch.randn((B, T, di), generator=g, device="cuda") if with_idx else None
     gate = None
     if with_gate:
-        gate = torch.randn(tuple(inp["q"].shape), generator=g, device="cuda")
+        gate = torch.randn((B,) + tuple(inp["q"].shape[1:]), generator=g, device="cuda")
         gate = gate.to(torch.float16 if inp["q_dtype"] == "f16" else torch.float32)
     return k_new, v_new, i_new, gate
 
@@ -176,3 +176,53 @@ def test_step_matches_oracle(orc, cfg, B, tile):
                      ref["n_sel"])
     want = orc.merge_gated(ref["pm"], ref["pl"], ref["po"], gate[check])
     assert_out_close(out.cpu().numpy()[check], want, f"{cfg} step")
+
+
+def test_bench_decode_step_configuration(orc):
+    """The decode step as the benchmark times it: 512 problems (8 distinct
+    seeded caches tiled over the batch), the cell-interleaved cache record
+    (1088 bytes per cell), seeded new rows appended, one qsa_step
+    call.  Eight problems spread over the batch are checked against the
+    oracle (appended codes and scales, ids bit for bit, gated output)."""
+    import bench
+    B, nd = 512, 8
+    base = make_inputs("decode", seed=1234, batch=nd)
+    dev = {}
+    for key in ARRAYS:
+        t = torch.from_numpy(base[key]).cuda()
+        dev[key] = t.repeat((B // nd,) + (1,) * (t.dim() - 1)).contiguous()
+    inp = dict(base)
+    inp["batch"] = B
+    N, Hkv, D, P = inp["N"], inp["Hkv"], inp["D"], inp["P"]
+    dev, strides = bench.interleave_cache(dev, B, N, Hkv, D)
+    say(f"[bench step] decode B={B} record={strides['kq_cell_stride']} B")
+    path = qsa.path_for(inp, P=P, strides=strides)
+    rows = _new_rows(inp, 4321, True, True)
+    k_new, v_new, i_new, gate = rows
+    adesc = qsa.append_desc(batch=B, T=inp["T"], n_cells=N, pos0=inp["pos0"], Hkv=Hkv, D=D,
+                            d_idx=inp["di"], strides=strides)
+    ws = torch.empty(qsa.qsa_step_workspace(path.idesc, path.adesc) // 4 + 64,
+                     dtype=torch.int32, device="cuda")
+    qsa.qsa_step(adesc, path.idesc, path.adesc, k_new, v_new, i_new, dev["Kq"], dev["Ksc"],
+                 dev["Vq"], dev["Vsc"], dev["K_idx"], dev["q_idx"], dev["q"], gate, path.ids,
+                 path.n_sel, path.out, ws)
+    torch.cuda.synchronize()
+    check = [0, 1, 77, 200, 255, 256, 400, 511]
+    sub = {k: (base[k][[b % nd for b in check]] if k in ARRAYS else base[k]) for k in base}
+    sub["batch"] = len(check)
+    kn, vn, inew, g = (r.cpu().numpy()[check] for r in rows)
+    rK, rKs, rV, rVs, rI = orc.kv_append(kn, vn, inew, sub["Kq"], sub["Ksc"], sub["Vq"],
+                                         sub["Vsc"], sub["K_idx"], pos0=inp["pos0"])
+    got = {name: dev[name].cpu().numpy()[check] for name in ("Kq", "Ksc", "Vq", "Vsc", "K_idx")}
+    assert np.array_equal(got["Kq"].reshape(rK.shape), rK)
+    assert np.array_equal(got["Vq"].reshape(rV.shape), rV)
+    assert np.array_equal(got["Ksc"].view(np.uint16).reshape(rKs.shape), rKs)
+    assert np.array_equal(got["Vsc"].view(np.uint16).reshape(rVs.shape), rVs)
+    assert np.array_equal(got["K_idx"].view(np.uint16), rI)
+    sub.update(Kq=rK, Ksc=rKs.view(np.float16), Vq=rV, Vsc=rVs.view(np.float16),
+               K_idx=rI.view(np.float16))
+    ref = orc.run(sub, P=P, scale=1.0 / math.sqrt(D))
+    assert_ids_equal(path.ids.cpu().numpy()[check], path.n_sel.cpu().numpy()[check], ref["ids"],
+                     ref["n_sel"])
+    want = orc.merge_gated(ref["pm"], ref["pl"], ref["po"], g)
+    assert_out_close(path.out.cpu().numpy()[check], want, "bench decode step")

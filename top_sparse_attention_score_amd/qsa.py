@@ -129,6 +129,81 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+# ------------------------------------------------------ size validation ---
+#
+# The library receives raw pointers and cannot see how large a buffer is; a
+# tensor shorter than the descriptor says would be read or written past its
+# end on the GPU.  Every call therefore checks, before anything is enqueued,
+# that each tensor's storage holds at least the bytes the descriptor
+# addresses from its data pointer on, and then that every tensor is on the
+# GPU.
+
+def _avail(t) -> int:
+    st = t.untyped_storage()
+    return st.nbytes() - (t.data_ptr() - st.data_ptr())
+
+
+def _need(t, nbytes: int, what: str, optional: bool = False) -> None:
+    if t is None:
+        if optional:
+            return
+        raise QsaError(f"{what}: missing tensor")
+    if _avail(t) < nbytes:
+        raise QsaError(f"{what}: tensor holds {_avail(t)} bytes from its start, "
+                       f"the call addresses {nbytes}")
+
+
+def _on_gpu(what: str, *tensors) -> None:
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise QsaError(f"{what}: not a GPU tensor")
+
+
+def _esize(dtype_code: int) -> int:
+    return 2 if dtype_code == QSA_F16 else 4
+
+
+def _cache_bytes(d, name: str, per_cell: int, cell_dense: int) -> int:
+    cs = getattr(d, f"{name}_cell_stride") or cell_dense
+    bs = getattr(d, f"{name}_batch_stride") or d.n_cells * cs
+    return (d.batch - 1) * bs + (d.n_cells - 1) * cs + per_cell
+
+
+def _check_cache(d, Kq, Ksc, Vq, Vsc) -> None:
+    codes, scales = d.Hkv * d.D, d.Hkv * (d.D // 32) * 2
+    _need(Kq, _cache_bytes(d, "kq", codes, codes), "Kq")
+    _need(Ksc, _cache_bytes(d, "ksc", scales, scales), "Ksc")
+    _need(Vq, _cache_bytes(d, "vq", codes, codes), "Vq")
+    _need(Vsc, _cache_bytes(d, "vsc", scales, scales), "Vsc")
+
+
+def _check_index(d, q_idx, K_idx, ids, n_sel) -> None:
+    _need(q_idx, d.batch * d.T * d.d_idx * 2, "q_idx")
+    _need(K_idx, d.batch * d.n_cells * d.d_idx * 2, "K_idx")
+    _need(ids, d.batch * d.T * d.ids_cap * 4, "ids")
+    _need(n_sel, d.batch * d.T * 4, "n_sel")
+
+
+def _check_attn(d, q, ids, n_sel, gate=None, out=None, gate_optional=True) -> None:
+    rows = d.batch * d.T * d.Hq * d.D
+    _need(q, rows * _esize(d.q_dtype), "q")
+    _need(ids, d.batch * d.T * d.ids_cap * 4, "ids")
+    _need(n_sel, d.batch * d.T * 4, "n_sel")
+    _need(gate, rows * _esize(d.q_dtype), "gate", optional=gate_optional)
+    if out is not None:
+        _need(out, rows * _esize(d.out_dtype), "out")
+
+
+def _check_append(d, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx) -> None:
+    rows = d.batch * d.T * d.Hkv * d.D * 4
+    _need(k_new, rows, "k_new")
+    _need(v_new, rows, "v_new")
+    _need(kidx_new, d.batch * d.T * d.d_idx * 4, "kidx_new", optional=True)
+    _check_cache(d, Kq, Ksc, Vq, Vsc)
+    if kidx_new is not None:
+        _need(K_idx, d.batch * d.n_cells * d.d_idx * 2, "K_idx")
+
+
 # ----------------------------------------------------------- descriptors ---
 
 def index_desc(*, batch: int, T: int, n_cells: int, d_idx: int, k: int, pos0: int,
@@ -170,35 +245,54 @@ def qsa_partials_floats(desc: AttnDesc) -> int:
 # ----------------------------------------------------------------- calls ---
 
 def qsa_index_topk(desc: IndexDesc, q_idx, K_idx, ids, n_sel, ws, stream=None) -> None:
+    _check_index(desc, q_idx, K_idx, ids, n_sel)
+    _on_gpu("qsa_index_topk", q_idx, K_idx, ids, n_sel, ws)
     _check(lib().qsa_index_topk(ctypes.byref(desc), _ptr(q_idx), _ptr(K_idx), _ptr(ids),
                                 _ptr(n_sel), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "qsa_index_topk")
 
 
 def qsa_index_topk_noalloc(desc: IndexDesc, q_idx, K_idx, ids, n_sel, stream=None) -> None:
+    _check_index(desc, q_idx, K_idx, ids, n_sel)
+    _on_gpu("qsa_index_topk_noalloc", q_idx, K_idx, ids, n_sel)
     _check(lib().qsa_index_topk_noalloc(ctypes.byref(desc), _ptr(q_idx), _ptr(K_idx), _ptr(ids),
                                         _ptr(n_sel), _stream(stream)), "qsa_index_topk_noalloc")
 
 
 def qsa_attend(desc: AttnDesc, q, Kq, Ksc, Vq, Vsc, ids, n_sel, partials,
                stream=None) -> None:
+    _check_attn(desc, q, ids, n_sel)
+    _check_cache(desc, Kq, Ksc, Vq, Vsc)
+    _need(partials, qsa_partials_floats(desc) * 4, "partials")
+    _on_gpu("qsa_attend", q, Kq, Ksc, Vq, Vsc, ids, n_sel, partials)
     _check(lib().qsa_attend(ctypes.byref(desc), _ptr(q), _ptr(Kq), _ptr(Ksc), _ptr(Vq),
                             _ptr(Vsc), _ptr(ids), _ptr(n_sel), _ptr(partials),
                             _stream(stream)), "qsa_attend")
 
 
 def qsa_merge(desc: AttnDesc, partials, out, stream=None) -> None:
+    _need(partials, qsa_partials_floats(desc) * 4, "partials")
+    _need(out, desc.batch * desc.T * desc.Hq * desc.D * _esize(desc.out_dtype), "out")
+    _on_gpu("qsa_merge", partials, out)
     _check(lib().qsa_merge(ctypes.byref(desc), _ptr(partials), _ptr(out), _stream(stream)),
            "qsa_merge")
 
 
 def qsa_merge_gated(desc: AttnDesc, partials, gate, out, stream=None) -> None:
+    _need(partials, qsa_partials_floats(desc) * 4, "partials")
+    rows = desc.batch * desc.T * desc.Hq * desc.D
+    _need(gate, rows * _esize(desc.q_dtype), "gate", optional=True)
+    _need(out, rows * _esize(desc.out_dtype), "out")
+    _on_gpu("qsa_merge_gated", partials, gate, out)
     _check(lib().qsa_merge_gated(ctypes.byref(desc), _ptr(partials), _ptr(gate), _ptr(out),
                                  _stream(stream)), "qsa_merge_gated")
 
 
 def qsa_attend_merge(desc: AttnDesc, q, Kq, Ksc, Vq, Vsc, ids, n_sel, gate, out,
                      stream=None) -> None:
+    _check_attn(desc, q, ids, n_sel, gate, out)
+    _check_cache(desc, Kq, Ksc, Vq, Vsc)
+    _on_gpu("qsa_attend_merge", q, Kq, Ksc, Vq, Vsc, ids, n_sel, gate, out)
     _check(lib().qsa_attend_merge(ctypes.byref(desc), _ptr(q), _ptr(Kq), _ptr(Ksc), _ptr(Vq),
                                   _ptr(Vsc), _ptr(ids), _ptr(n_sel), _ptr(gate), _ptr(out),
                                   _stream(stream)), "qsa_attend_merge")
@@ -206,9 +300,23 @@ def qsa_attend_merge(desc: AttnDesc, q, Kq, Ksc, Vq, Vsc, ids, n_sel, gate, out,
 
 def qsa_kv_append(desc: AppendDesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
                   stream=None) -> None:
+    _check_append(desc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx)
+    _on_gpu("qsa_kv_append", k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx)
     _check(lib().qsa_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(kidx_new),
                                _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc), _ptr(K_idx),
                                _stream(stream)), "qsa_kv_append")
+
+
+def _check_step(pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, q_idx,
+                q, gate, ids, n_sel, out, ws, ws_need) -> None:
+    _check_append(pdesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx)
+    _check_index(idesc, q_idx, K_idx, ids, n_sel)
+    _check_attn(adesc, q, ids, n_sel, gate, out)
+    _check_cache(adesc, Kq, Ksc, Vq, Vsc)
+    if ws_need:
+        _need(ws, ws_need, "workspace")
+    _on_gpu("the step", k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, q_idx, q, gate, ids,
+            n_sel, out, ws)
 
 
 def qsa_decode_window_workspace(idesc: IndexDesc, adesc: AttnDesc) -> int:
@@ -218,6 +326,8 @@ def qsa_decode_window_workspace(idesc: IndexDesc, adesc: AttnDesc) -> int:
 def qsa_decode_window(pdesc: AppendDesc, idesc: IndexDesc, adesc: AttnDesc, k_new, v_new,
                       kidx_new, Kq, Ksc, Vq, Vsc, K_idx, q_idx, q, gate, ids, n_sel, out, ws,
                       stream=None) -> None:
+    _check_step(pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, q_idx, q,
+                gate, ids, n_sel, out, ws, qsa_decode_window_workspace(idesc, adesc))
     _check(lib().qsa_decode_window(
         ctypes.byref(pdesc), ctypes.byref(idesc), ctypes.byref(adesc), _ptr(k_new), _ptr(v_new),
         _ptr(kidx_new), _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc), _ptr(K_idx), _ptr(q_idx),
@@ -232,6 +342,8 @@ def qsa_step_workspace(idesc: IndexDesc, adesc: AttnDesc) -> int:
 
 def qsa_step(pdesc: AppendDesc, idesc: IndexDesc, adesc: AttnDesc, k_new, v_new, kidx_new, Kq,
              Ksc, Vq, Vsc, K_idx, q_idx, q, gate, ids, n_sel, out, ws, stream=None) -> None:
+    _check_step(pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, q_idx, q,
+                gate, ids, n_sel, out, ws, qsa_step_workspace(idesc, adesc))
     _check(lib().qsa_step(
         ctypes.byref(pdesc), ctypes.byref(idesc), ctypes.byref(adesc), _ptr(k_new), _ptr(v_new),
         _ptr(kidx_new), _ptr(Kq), _ptr(Ksc), _ptr(Vq), _ptr(Vsc), _ptr(K_idx), _ptr(q_idx),
@@ -246,6 +358,8 @@ class StepCall:
 
     def __init__(self, pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
                  q_idx, q, gate, ids, n_sel, out, ws, stream=None):
+        _check_step(pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx, q_idx,
+                    q, gate, ids, n_sel, out, ws, qsa_step_workspace(idesc, adesc))
         self._keep = (pdesc, idesc, adesc, k_new, v_new, kidx_new, Kq, Ksc, Vq, Vsc, K_idx,
                       q_idx, q, gate, ids, n_sel, out, ws)
         self._args = (ctypes.byref(pdesc), ctypes.byref(idesc), ctypes.byref(adesc),
