@@ -406,6 +406,11 @@ QSA_API int qsa_decode_window(const qsa_append_desc* pdesc, const qsa_index_desc
  *     problem one workgroup (one token per problem, batch >= 128, rows of
  *     at most 16384 cells, some token selecting): that workgroup writes its
  *     problem's new token, then scans the keys;
+ *   - with one token per problem otherwise (fewer problems, or longer
+ *     rows; some token selecting; Hkv * D <= 512), the append runs inside
+ *     the chip-wide key scan: the workgroup whose rows end with the new cell
+ *     writes the problem's new token (not for rows of 65537 to 262144 cells
+ *     with k <= 4096, whose index path starts with a sampling kernel);
  *   - the merge and the gate run inside the attention kernel with the
  *     matrix kernel when P is 1, 2 or 4 (as qsa_attend_merge), and when P
  *     is a multiple of 4 above 4 with batch * T * Hkv >= 512 (the kernel then

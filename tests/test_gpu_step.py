@@ -5,7 +5,8 @@ scales, index keys), ids, n_sel and the output must be equal bit for bit.
 
 The cases cover each way the step folds calls: the append inside the
 decode scan/select kernel (one token, 128 or more problems, rows of at most
-16384 cells) or as its own kernel; the merge inside the attention kernel
+16384 cells), inside the chip-wide one-token scan (fewer problems) or as its
+own kernel; the merge inside the attention kernel
 (P in {1, 2, 4}; P a multiple of 4 with 512 or more (token, KV head) pairs)
 or as its own kernel (other splits, the vector kernel); dense rows; the
 draft, long and prompt-chunk index paths; fp16 queries and outputs; no index
@@ -40,8 +41,10 @@ CASES = [
     ("decode", 128, 4, True, True, dict(tile=4)),     # append in the scan, merge in attention
     ("decode", 160, 8, True, True, dict(tile=4)),     # append in the scan, separate merge
     ("decode", 128, 4, False, False, dict(tile=4)),   # no gate, no new index key
-    ("decode", 2, 4, True, True, {}),                 # separate append, merge in attention
-    ("decode", 3, 16, True, True, {}),                # all four calls separate
+    ("decode", 2, 4, True, True, {}),                 # append in the chip-wide scan, merge in attention
+    ("decode", 3, 4, True, False, {}),                # the same without a new index key
+    ("decode", 1, 32, True, True, {}),                # one problem: append in the scan, merge apart
+    ("decode", 3, 16, True, True, {}),                # append in the chip-wide scan, separate merge
     ("decode", 2, 2, True, True, dict(pos0=1500)),    # dense rows
     ("tiny", 5, 4, True, True, {}),
     ("tiny", 130, 1, True, True, dict(tile=5)),       # append in the scan, P = 1

@@ -56,6 +56,61 @@ __global__ __launch_bounds__(256) void k_idx_scan(const uint4* __restrict__ q_id
     idx_scan_block<DI, TT>(blockIdx.x, blockIdx.y, q_idx, K_idx, keys, T, N, nvis_max);
 }
 
+// k_idx_scan for one token with the step's append folded in (qsa_step with
+// fewer problems than the fused scan/select takes).  The workgroup whose
+// rows end with the new cell (the last visible row, pos0) also writes the
+// problem's new token: the new fp32 K/V rows are loaded at the start and
+// written as codes and scales after the scan by the quantisation lanes of
+// qsa_kv_append; the scan skips the new cell's row (its old contents) and
+// wave 0 scores the new fp16 key with the scan's own dot2 sequence and row
+// reduction -- the score the scan would compute from the written key --
+// and writes the key.  Needs Hkv * D / 2 <= 256 quantisation lanes.
+template <int DI>
+__global__ __launch_bounds__(256) void k_idx_scan_append(const uint4* __restrict__ q_idx,
+                                                         const uint4* __restrict__ K_idx,
+                                                         uint32_t* __restrict__ keys, int N,
+                                                         int nvis, AppendLaunch ap)
+{
+    constexpr int LPR = DI / 8;   // lanes per key row
+    const int bx = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, sub = tid % LPR;
+    const int jnew = nvis - 1;
+    const bool owner = jnew / idx_scan_rows_per_block<DI>() == bx;
+    const bool newkey = owner && ap.kidx_new != nullptr;
+    const long long nq = (long long)ap.Hkv * (ap.D / 32) * 16;
+    const bool qlane = owner && tid < nq;
+    const long long wq = (long long)b * nq + tid;
+    float4 nv = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint4 nkey = make_uint4(0u, 0u, 0u, 0u);
+    if (qlane)
+        nv = append_quant_load(ap, wq);
+    if (newkey && tid < LPR) {
+        const float4* src = (const float4*)(ap.kidx_new + (size_t)b * DI) + 2 * sub;
+        const float4 x0 = src[0], x1 = src[1];
+        nkey = make_uint4(pack_half2_rne(x0.x, x0.y), pack_half2_rne(x0.z, x0.w),
+                          pack_half2_rne(x1.x, x1.y), pack_half2_rne(x1.z, x1.w));
+    }
+    idx_scan_rows<DI, 1>(bx, b, q_idx, K_idx, 1, N, nvis, [&](int, int j, float sc) {
+        if (!(newkey && j == jnew))
+            keys[(size_t)b * N + j] = score_key(sc);
+    });
+    if (newkey && tid < 64) {
+        const uint4 qv = q_idx[(size_t)b * (DI / 8) + sub];
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint32_t kw[4] = {nkey.x, nkey.y, nkey.z, nkey.w};
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
+        acc = row_sum<LPR>(acc);
+        if (tid == 0)
+            keys[(size_t)b * N + jnew] = score_key(acc);
+        if (tid < LPR)
+            *((uint4*)(ap.K_idx + ((size_t)b * ap.N + ap.pos0) * DI) + sub) = nkey;
+    }
+    if (qlane)
+        append_quant_store(ap, wq, nv, true);  // whole 8-lane groups (nq % 16 == 0)
+}
+
 // A few tokens (2 <= T <= 16) against every visible cell on the matrix
 // cores: a wave takes 16 consecutive cells per group; C[token][cell] =
 // sum_d q[token][d] K[cell][d] with v_mfma_f32_16x16x32_f16 (A = the T
@@ -1721,6 +1776,16 @@ static void launch_scan(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipS
 }
 
 template <int DI>
+static void launch_scan_append(const IndexLaunch& a, uint32_t* keys, int nvis_max,
+                               const AppendLaunch& ap, hipStream_t s)
+{
+    constexpr int rows_per_block = (256 / (DI / 8)) * 8;
+    dim3 grid((nvis_max + rows_per_block - 1) / rows_per_block, a.B);
+    k_idx_scan_append<DI><<<grid, 256, 0, s>>>((const uint4*)a.q_idx, (const uint4*)a.K_idx,
+                                               keys, a.N, nvis_max, ap);
+}
+
+template <int DI>
 static void launch_gemm(const IndexLaunch& a, uint32_t* keys, int nvis_max, hipStream_t s)
 {
     constexpr int cells_per_block = 4 * 32 * kGemmBlocks;
@@ -1770,8 +1835,14 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLa
 #undef QSA_FUSED
         return hipGetLastError();
     }
+    // One token through the chip-wide scan: the workgroup holding the new
+    // cell's row writes the new token while its quantisation lanes fit.
+    const bool long1 = any_select && a.T == 1 && a.N > kRowThreads * 64 &&
+                       a.N <= kLongFusedMaxCells && a.k <= kCandCap / 2;
+    const bool scan_fold = ap && any_select && a.T == 1 && !long1 && ap->T == 1 &&
+                           (long long)ap->Hkv * ap->D / 2 <= 256;
     // Every other path: the append as its own kernel first.
-    if (ap) {
+    if (ap && !scan_fold) {
         const hipError_t e = launch_kv_append(*ap, s);
         if (e != hipSuccess)
             return e;
@@ -1808,8 +1879,6 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLa
     // One token against a row too long for the register select: sampled
     // bound, then the chip-wide scan keeps only the candidates, then the
     // exact select among them (no key array, no chip-wide select).
-    const bool long1 = any_select && a.T == 1 && a.N > kRowThreads * 64 &&
-                       a.N <= kLongFusedMaxCells && a.k <= kCandCap / 2;
     if (long1) {
         const dim3 gs(kSampleCells / 256, 1, a.B);
         const _Float16* q = (const _Float16*)a.q_idx;
@@ -1833,7 +1902,12 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s, const AppendLa
         return hipGetLastError();
     }
     if (any_select) {
-        if (a.T == 1) {
+        if (a.T == 1 && scan_fold) {
+            if (a.DI == 64)
+                launch_scan_append<64>(a, w.keys, nvis_max, *ap, s);
+            else
+                launch_scan_append<128>(a, w.keys, nvis_max, *ap, s);
+        } else if (a.T == 1) {
             if (a.DI == 64)
                 launch_scan<64>(a, w.keys, nvis_max, s);
             else
