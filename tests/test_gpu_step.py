@@ -44,6 +44,7 @@ CASES = [
     ("decode", 2, 4, True, True, {}),                 # append in the chip-wide scan, merge in attention
     ("decode", 3, 4, True, False, {}),                # the same without a new index key
     ("decode", 1, 32, True, True, {}),                # one problem: append in the scan, merge apart
+    ("decode", 2, 4, True, True, dict(N=65536)),      # the same over 65536 cells (64 keys a thread)
     ("decode", 3, 16, True, True, {}),                # append in the chip-wide scan, separate merge
     ("decode", 2, 2, True, True, dict(pos0=1500)),    # dense rows
     ("tiny", 5, 4, True, True, {}),
