@@ -35,6 +35,9 @@ ARRAYS = ("q_idx", "K_idx", "q", "Kq", "Ksc", "Vq", "Vsc")
 
 PROMPT_SMALL = dict(T=64, N=4096, di=128, k=256, dense_max=259, Hq=24, Hkv=2, D=256, P=1,
                     q_dtype="f16", out_dtype="f16", heavy_tail=False)
+# many tokens through the sampled-bound index (rows of 16384 cells and more)
+PROMPT_MID = dict(T=128, N=16384, di=128, k=2048, dense_max=2051, Hq=24, Hkv=2, D=256, P=1,
+                  q_dtype="f16", out_dtype="f16", heavy_tail=False)
 
 # (config, batch, P, gate, append index keys, overrides)
 CASES = [
@@ -52,6 +55,8 @@ CASES = [
     ("draft", 2, 16, True, True, {}),
     ("long", 1, 64, True, True, dict(pos0=100000)),
     ("prompt_small", 1, 1, True, True, {}),
+    ("prompt_mid", 1, 1, True, True, {}),             # sampled-bound index, many tokens
+    ("prompt_mid", 2, 1, False, False, {}),           # the same without new index keys
     ("prompt_small", 1, 4, False, True, {}),
     ("decode", 3, 4, True, True, dict(algo=qsa.QSA_ATTEND_VECTOR)),   # vector kernel: merge apart
     ("decode", 128, 8, True, True, dict(tile=4, algo=qsa.QSA_ATTEND_VECTOR)),
@@ -62,7 +67,7 @@ def _inputs(cfg, seed, B, over):
     over = dict(over)
     tile = over.pop("tile", None)
     over.pop("algo", None)
-    c = PROMPT_SMALL if cfg == "prompt_small" else cfg
+    c = {"prompt_small": PROMPT_SMALL, "prompt_mid": PROMPT_MID}.get(cfg, cfg)
     if tile is None:
         return make_inputs(c, seed=seed, batch=B, **over)
     inp = make_inputs(c, seed=seed, batch=tile, **over)
