@@ -56,6 +56,39 @@ __global__ __launch_bounds__(256) void k_idx_scan(const uint4* __restrict__ q_id
     idx_scan_block<DI, TT>(blockIdx.x, blockIdx.y, q_idx, K_idx, keys, T, N, nvis_max);
 }
 
+// The new index key of a one-token append, as the scan kernels that fold
+// the append in handle it: lane `sub` of a key-row group holds 16 bytes of
+// the key (the new fp32 row rounded to fp16, nearest even, as qsa_kv_append
+// writes it); the group scores it with the scan's own dot2 sequence and
+// row reduction, so the score equals the one the scan computes from the
+// written key.
+template <int DI>
+__device__ __forceinline__ uint4 new_key_slice(const AppendLaunch& ap, int b, int sub)
+{
+    const float4* src = (const float4*)(ap.kidx_new + (size_t)b * DI) + 2 * sub;
+    const float4 x0 = src[0], x1 = src[1];
+    return make_uint4(pack_half2_rne(x0.x, x0.y), pack_half2_rne(x0.z, x0.w),
+                      pack_half2_rne(x1.x, x1.y), pack_half2_rne(x1.z, x1.w));
+}
+
+template <int DI>
+__device__ __forceinline__ float new_key_score(const uint32_t (&qw)[4], uint4 nkey)
+{
+    const uint32_t kw[4] = {nkey.x, nkey.y, nkey.z, nkey.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
+    return row_sum<DI / 8>(acc);
+}
+
+// Slice `sub` of the new key into its cache row (cell pos0 of problem b).
+template <int DI>
+__device__ __forceinline__ void write_new_key(const AppendLaunch& ap, int b, int sub, uint4 nkey)
+{
+    *((uint4*)(ap.K_idx + ((size_t)b * ap.N + ap.pos0) * DI) + sub) = nkey;
+}
+
 // k_idx_scan for one token with the step's append folded in (qsa_step with
 // fewer problems than the fused scan/select takes).  The workgroup whose
 // rows end with the new cell (the last visible row, pos0) also writes the
@@ -83,29 +116,20 @@ __global__ __launch_bounds__(256) void k_idx_scan_append(const uint4* __restrict
     uint4 nkey = make_uint4(0u, 0u, 0u, 0u);
     if (qlane)
         nv = append_quant_load(ap, wq);
-    if (newkey && tid < LPR) {
-        const float4* src = (const float4*)(ap.kidx_new + (size_t)b * DI) + 2 * sub;
-        const float4 x0 = src[0], x1 = src[1];
-        nkey = make_uint4(pack_half2_rne(x0.x, x0.y), pack_half2_rne(x0.z, x0.w),
-                          pack_half2_rne(x1.x, x1.y), pack_half2_rne(x1.z, x1.w));
-    }
+    if (newkey && tid < LPR)
+        nkey = new_key_slice<DI>(ap, b, sub);
     idx_scan_rows<DI, 1>(bx, b, q_idx, K_idx, 1, N, nvis, [&](int, int j, float sc) {
         if (!(newkey && j == jnew))
             keys[(size_t)b * N + j] = score_key(sc);
     });
-    if (newkey && tid < 64) {
+    if (newkey && tid < 64) {   // wave 0: lanes 0 .. LPR-1 hold the key
         const uint4 qv = q_idx[(size_t)b * (DI / 8) + sub];
         const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-        const uint32_t kw[4] = {nkey.x, nkey.y, nkey.z, nkey.w};
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
-        acc = row_sum<LPR>(acc);
+        const float acc = new_key_score<DI>(qw, nkey);
         if (tid == 0)
             keys[(size_t)b * N + jnew] = score_key(acc);
         if (tid < LPR)
-            *((uint4*)(ap.K_idx + ((size_t)b * ap.N + ap.pos0) * DI) + sub) = nkey;
+            write_new_key<DI>(ap, b, sub, nkey);
     }
     if (qlane)
         append_quant_store(ap, wq, nv, true);  // whole 8-lane groups (nq % 16 == 0)
@@ -929,12 +953,8 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
     if constexpr (APPEND) {
         if (qlane)
             nv = append_quant_load(ap, wq);
-        if (newkey && tid < 64) {
-            const float4* src = (const float4*)(ap.kidx_new + (size_t)b * DI) + 2 * sub;
-            const float4 x0 = src[0], x1 = src[1];
-            nkey = make_uint4(pack_half2_rne(x0.x, x0.y), pack_half2_rne(x0.z, x0.w),
-                              pack_half2_rne(x1.x, x1.y), pack_half2_rne(x1.z, x1.w));
-        }
+        if (newkey && tid < 64)
+            nkey = new_key_slice<DI>(ap, b, sub);
     }
     const int jnew = newkey ? nvis - 1 : -1;  // the new cell: scored after the scan
     // The select's first-digit histogram is counted as the keys are made.
@@ -970,19 +990,14 @@ __global__ __launch_bounds__(kRowThreads) void k_scan_select(const uint4* __rest
     if constexpr (APPEND) {
         if (newkey && tid < 64) {
             // wave 0: the new cell's score as the loop computes it
-            const uint32_t kw[4] = {nkey.x, nkey.y, nkey.z, nkey.w};
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc = __builtin_amdgcn_fdot2(as_half2(qw[e]), as_half2(kw[e]), acc, false);
-            acc = row_sum<LPR>(acc);
+            const float acc = new_key_score<DI>(qw, nkey);
             if (tid == 0) {
                 const uint32_t kk = score_key(acc);
                 keys_s[jnew] = kk;
                 atomicAdd(&hist[kk >> 21], 1u);
             }
             if (tid < LPR)
-                *((uint4*)(ap.K_idx + ((size_t)b * ap.N + ap.pos0) * DI) + sub) = nkey;
+                write_new_key<DI>(ap, b, sub, nkey);
         }
         if (qlane)
             append_quant_store(ap, wq, nv, true);  // whole 8-lane groups (nq % 16 == 0)
